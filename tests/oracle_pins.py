@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: facts fixed by the mathematics or printed on the
+pages, independent of the oracle's own code.
+
+Each pin is a function that raises AssertionError when the oracle disagrees.
+They look the oracle's functions up through the ``oracle.ref`` module at call
+time, so a test can plant a mistake in the oracle (monkeypatch) and check that
+some pin catches it.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import synth
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pages_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _dec(bits):
+    return ref.bf16_bits_to_f64(bits)
+
+
+def _bits_of(value: float) -> np.uint16:
+    return synth.f32_to_bf16_bits(np.array([value], dtype=np.float32))[0]
+
+
+def _rand(shape, seed, tag=91):
+    return synth.normal_bf16(shape, seed, tag)
+
+
+# ----------------------------------------------------------------- attention
+
+def pin_identical_keys():
+    """All keys equal k: every weight is 1/S_kv, so O_i = mean_j v_j and
+    LSE_i = scale * q_i.k + ln S_kv (closed form)."""
+    B, Sq, Skv, H, D = 2, 37, 53, 3, 64
+    q = _rand((B, Sq, H, D), 1)
+    krow = _rand((B, 1, H, D), 2)
+    k = np.repeat(krow, Skv, axis=1)
+    v = _rand((B, Skv, H, D), 3)
+    O, L = ref.attention(q, k, v)
+    assert O.shape == (B, Sq, H, D) and L.shape == (B, H, Sq)
+    vm = _dec(v).mean(axis=1)                                   # [B,H,D]
+    exp_o = np.broadcast_to(vm[:, None, :, :], O.shape)
+    assert np.allclose(O, exp_o, rtol=0, atol=1e-12), "identical keys: O != mean(V)"
+    qk = np.sum(_dec(q) * _dec(krow), axis=3)                   # [B,Sq,H]
+    exp_l = np.transpose(qk / math.sqrt(D) + math.log(Skv), (0, 2, 1))
+    assert np.allclose(L, exp_l, rtol=0, atol=1e-12), "identical keys: LSE closed form"
+
+
+def pin_dominant_logit():
+    """q = 2*ones, K = 0 except K[j*] = 2*ones (D = 128): the logit of j* is
+    s* = 4*sqrt(128) and every other logit is 0, so
+    O = (e^{s*} v_{j*} + sum_{j != j*} v_j) / (e^{s*} + S - 1) and
+    LSE = s* + ln(1 + (S - 1) e^{-s*})."""
+    S, D, H = 300, 128, 2
+    two = _bits_of(2.0)
+    q = np.full((1, 7, H, D), two, dtype=np.uint16)
+    k = np.zeros((1, S, H, D), dtype=np.uint16)
+    js = [123, 7]
+    for h in range(H):
+        k[0, js[h], h, :] = two
+    v = _rand((1, S, H, D), 4)
+    O, L = ref.attention(q, k, v)
+    s_star = 4.0 * math.sqrt(D)
+    vf = _dec(v)
+    for h in range(H):
+        others = vf[0, :, h, :].sum(axis=0) - vf[0, js[h], h, :]
+        e = math.exp(s_star)
+        exp_o = (e * vf[0, js[h], h, :] + others) / (e + S - 1)
+        assert np.allclose(O[0, :, h, :], exp_o[None, :], rtol=0, atol=1e-13), "dominant logit: O"
+        exp_l = s_star + math.log1p((S - 1) * math.exp(-s_star))
+        assert np.allclose(L[0, h, :], exp_l, rtol=0, atol=1e-12), "dominant logit: LSE"
+
+
+def pin_rows_sum_to_one():
+    """Softmax rows are non-negative and sum to 1; V = 1 everywhere gives O = 1."""
+    B, Sq, Skv, H, D = 1, 19, 41, 2, 64
+    q = _rand((B, Sq, H, D), 5)
+    k = _rand((B, Skv, H, D), 6)
+    p = ref.attention_probs(q, k, 0, 1, range(Sq))
+    assert p.shape == (Sq, Skv)
+    assert np.all(p >= 0) and np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    ones = np.full((B, Skv, H, D), _bits_of(1.0), dtype=np.uint16)
+    O, _ = ref.attention(q, k, ones)
+    assert np.allclose(O, 1.0, rtol=0, atol=1e-13), "V = 1 must give O = 1"
+
+
+def pin_single_key():
+    """S_kv = 1: O = v_0 and LSE = scale * q . k_0."""
+    B, Sq, H, D = 2, 9, 3, 128
+    q = _rand((B, Sq, H, D), 7)
+    k = _rand((B, 1, H, D), 8)
+    v = _rand((B, 1, H, D), 9)
+    O, L = ref.attention(q, k, v)
+    assert np.array_equal(O, np.broadcast_to(_dec(v), O.shape)), "S_kv = 1: O = v_0"
+    s = np.sum(_dec(q) * _dec(k), axis=3) / math.sqrt(D)        # [B,Sq,H]
+    assert np.allclose(L, np.transpose(s, (0, 2, 1)), rtol=0, atol=1e-12)
+
+
+def pin_no_keys():
+    """S_kv = 0 (chosen reading): O = 0 and LSE = -inf, never NaN."""
+    q = _rand((1, 5, 2, 64), 10)
+    k = np.zeros((1, 0, 2, 64), dtype=np.uint16)
+    O, L = ref.attention(q, k, k)
+    assert np.all(O == 0) and np.all(np.isneginf(L))
+
+
+def pin_library_softmax():
+    """Against scipy's softmax and logsumexp on an asymmetric shape
+    (S_q != S_kv, H != D/..), logits formed with einsum."""
+    from scipy.special import logsumexp, softmax
+    B, Sq, Skv, H, D = 2, 23, 45, 3, 64
+    q = _rand((B, Sq, H, D), 11)
+    k = _rand((B, Skv, H, D), 12)
+    v = _rand((B, Skv, H, D), 13)
+    scale = 0.3
+    O, L = ref.attention(q, k, v, scale=scale)
+    logits = np.einsum("bqhd,bkhd->bhqk", _dec(q), _dec(k)) * scale
+    exp_l = logsumexp(logits, axis=3)
+    exp_o = np.einsum("bhqk,bkhd->bqhd", softmax(logits, axis=3), _dec(v))
+    assert np.allclose(L, exp_l, rtol=0, atol=1e-12), "LSE vs scipy logsumexp"
+    assert np.allclose(O, exp_o, rtol=0, atol=1e-12), "O vs scipy softmax"
+
+
+def pin_brute_force_tiny():
+    """Explicit loops in pure Python (no BLAS) on a tiny case."""
+    B, Sq, Skv, H, D = 1, 4, 6, 2, 4
+    q = _rand((B, Sq, H, D), 14)
+    k = _rand((B, Skv, H, D), 15)
+    v = _rand((B, Skv, H, D), 16)
+    O, L = ref.attention(q, k, v)
+    qf, kf, vf = _dec(q).tolist(), _dec(k).tolist(), _dec(v).tolist()
+    sc = 1.0 / math.sqrt(D)
+    for h in range(H):
+        for i in range(Sq):
+            logits = []
+            for j in range(Skv):
+                acc = 0.0
+                for d in range(D):
+                    acc += qf[0][i][h][d] * kf[0][j][h][d]
+                logits.append(acc * sc)
+            tot = sum(math.exp(x) for x in logits)
+            assert abs(L[0, h, i] - math.log(tot)) < 1e-12
+            for d in range(D):
+                o = sum(math.exp(logits[j]) * vf[0][j][h][d] for j in range(Skv)) / tot
+                assert abs(O[0, i, h, d] - o) < 1e-12
+
+
+def pin_permutation_and_scaling():
+    """Permuting keys and values together leaves O and LSE unchanged;
+    scaling V by 2 scales O by exactly 2."""
+    B, Sq, Skv, H, D = 1, 11, 40, 2, 64
+    q = _rand((B, Sq, H, D), 17)
+    k = _rand((B, Skv, H, D), 18)
+    v = _rand((B, Skv, H, D), 19)
+    O, L = ref.attention(q, k, v)
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(Skv)
+    O2, L2 = ref.attention(q, k[:, perm], v[:, perm])
+    assert np.allclose(O, O2, rtol=0, atol=1e-13) and np.allclose(L, L2, rtol=0, atol=1e-12)
+    O3, L3 = ref.attention(q, k, 2.0 * _dec(v))
+    assert np.array_equal(O3, 2.0 * O) and np.array_equal(L3, L)
+
+
+def pin_scale_argument():
+    """An explicit scale equal to 1/sqrt(D) gives the default result; doubling
+    the scale equals doubling Q (exact in bf16)."""
+    B, S, H, D = 1, 16, 2, 64
+    q = _rand((B, S, H, D), 20)
+    k = _rand((B, S, H, D), 21)
+    v = _rand((B, S, H, D), 22)
+    O, L = ref.attention(q, k, v)
+    Od, Ld = ref.attention(q, k, v, scale=1.0 / 8.0)
+    assert np.array_equal(O, Od) and np.array_equal(L, Ld)
+    O2, L2 = ref.attention(q, k, v, scale=0.25)
+    O3, L3 = ref.attention(2.0 * _dec(q), k, v)
+    assert np.allclose(O2, O3, rtol=0, atol=1e-12) and np.allclose(L2, L3, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- merge
+
+def _partials(q, k, v, bounds):
+    outs, lses = [], []
+    for lo, hi in bounds:
+        o, l = ref.attention(q, k[:, lo:hi], v[:, lo:hi])
+        outs.append(o)
+        lses.append(l)
+    return outs, lses
+
+
+def pin_merge_equals_full():
+    """Merging partials over disjoint key spans (one of them empty) equals
+    attention over all keys."""
+    B, Sq, Skv, H, D = 1, 256, 256, 2, 64
+    q, k, v = synth.tiny_qkv()
+    O, L = ref.attention(q, k, v)
+    bounds = [(0, 64), (64, 128), (128, 128), (128, 192), (192, 256)]
+    outs, lses = _partials(q, k, v, bounds)
+    Om, Lm = ref.merge(outs, lses)
+    assert np.allclose(Om, O, rtol=0, atol=1e-12) and np.allclose(Lm, L, rtol=0, atol=1e-12)
+    # the ragged, asymmetric case: S_q != S_kv, H != S
+    q2 = _rand((2, 13, 3, 64), 23)
+    k2 = _rand((2, 29, 3, 64), 24)
+    v2 = _rand((2, 29, 3, 64), 25)
+    O2, L2 = ref.attention(q2, k2, v2)
+    outs, lses = _partials(q2, k2, v2, [(0, 5), (5, 17), (17, 29)])
+    Om2, Lm2 = ref.merge(outs, lses)
+    assert np.allclose(Om2, O2, rtol=0, atol=1e-12) and np.allclose(Lm2, L2, rtol=0, atol=1e-12)
+
+
+def pin_merge_attention2d_grid():
+    """The pages' 2x3 Attention2D example: the row group holding query shards
+    {0,1,2} attends key shards {0,3}, {1,4}, {2,5}; merging the three partials
+    recovers full attention for those queries."""
+    g = _golden()["attention2d_grid"]
+    n, shard = g["shards"], 24
+    H, D = 2, 64
+    q = _rand((1, n * shard, H, D), 26)
+    k = _rand((1, n * shard, H, D), 27)
+    v = _rand((1, n * shard, H, D), 28)
+    rows = np.concatenate([np.arange(s * shard, (s + 1) * shard) for s in g["row_group_queries"]])
+    qrow = q[:, rows]
+    O, L = ref.attention(qrow, k, v)
+    outs, lses = [], []
+    for key_shards in g["row_group_key_shards"]:
+        keys = np.concatenate([np.arange(s * shard, (s + 1) * shard) for s in key_shards])
+        o, l = ref.attention(qrow, k[:, keys], v[:, keys])
+        outs.append(o)
+        lses.append(l)
+    assert len(outs) == g["col_size"]
+    Om, Lm = ref.merge(outs, lses)
+    assert np.allclose(Om, O, rtol=0, atol=1e-12) and np.allclose(Lm, L, rtol=0, atol=1e-12)
+
+
+def pin_merge_closed_forms():
+    """n identical partials: O unchanged, LSE + ln n.  A -inf partial has no
+    effect.  Equal LSEs average.  n = 1 is the identity.  All -inf: O = 0,
+    LSE = -inf."""
+    B, S, H, D = 1, 10, 3, 64
+    o1 = _dec(_rand((B, S, H, D), 29))
+    o2 = _dec(_rand((B, S, H, D), 30))
+    l1 = _dec(_rand((B, H, S), 31)) * 3.0 + 5.0
+    for n in (1, 2, 3, 8):
+        O, L = ref.merge([o1] * n, [l1] * n)
+        assert np.allclose(O, o1, rtol=0, atol=1e-13)
+        assert np.allclose(L, l1 + math.log(n), rtol=0, atol=1e-12)
+    ninf = np.full((B, H, S), -np.inf)
+    O, L = ref.merge([o1, o2], [l1, ninf])
+    assert np.allclose(O, o1, rtol=0, atol=1e-13) and np.array_equal(L, l1)
+    O, L = ref.merge([o2, o1], [ninf, l1])
+    assert np.allclose(O, o1, rtol=0, atol=1e-13) and np.array_equal(L, l1)
+    O, L = ref.merge([o1, o2], [l1, l1])
+    assert np.allclose(O, 0.5 * (o1 + o2), rtol=0, atol=1e-13)
+    assert np.allclose(L, l1 + math.log(2.0), rtol=0, atol=1e-12)
+    O, L = ref.merge([o1, o2], [ninf, ninf])
+    assert np.all(O == 0) and np.all(np.isneginf(L))
+    # weights are per (b, h, s): an asymmetric LSE pattern picks per row
+    lbig = l1.copy()
+    lbig[0, 1, 4] = 1e3
+    O, L = ref.merge([o1, o2], [lbig, l1])
+    assert np.allclose(O[0, 4, 1], o1[0, 4, 1], rtol=0, atol=1e-13)
+    assert np.allclose(O[0, 4, 0], 0.5 * (o1[0, 4, 0] + o2[0, 4, 0]), rtol=0, atol=1e-13)
+
+
+def pin_ring_streaming_merge():
+    """The Ring schedule's two-partial sigmoid/logsigmoid update, applied
+    block by block, equals the batched merge and full attention."""
+    q, k, v = synth.tiny_qkv()
+    O, L = ref.attention(q, k, v)
+    outs, lses = _partials(q, k, v, [(0, 64), (64, 128), (128, 192), (192, 256)])
+    run_o, run_l = outs[0], lses[0]
+    for o, l in zip(outs[1:], lses[1:]):
+        run_o, run_l = ref.merge_two_logsigmoid(run_o, run_l, o, l)
+    assert np.allclose(run_o, O, rtol=0, atol=1e-12) and np.allclose(run_l, L, rtol=0, atol=1e-12)
+    ninf = np.full_like(lses[0], -np.inf)
+    o, l = ref.merge_two_logsigmoid(outs[0], ninf, outs[1], lses[1])
+    assert np.allclose(o, outs[1], rtol=0, atol=1e-13) and np.array_equal(l, lses[1])
+    o, l = ref.merge_two_logsigmoid(outs[0], ninf, outs[1], ninf)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# ----------------------------------------------------------------- relayout
+
+def pin_relayout_index_map():
+    """Element-wise: Y[b, p*S_loc + s, j, d] = X_p[b, s, r*H/P + j, d],
+    checked by scalar lookups at random positions."""
+    B, S_loc, H, D, P = 2, 7, 8, 16, 4
+    chunks = [synth.random_bits16((B, S_loc, H, D), 100 + p) for p in range(P)]
+    g = np.random.Generator(np.random.PCG64(9))
+    for r in range(P):
+        y = ref.relayout_seq_to_head(chunks, P, r)
+        assert y.shape == (B, P * S_loc, H // P, D) and y.dtype == np.uint16
+        for _ in range(200):
+            b, p, s = int(g.integers(B)), int(g.integers(P)), int(g.integers(S_loc))
+            j, d = int(g.integers(H // P)), int(g.integers(D))
+            assert y[b, p * S_loc + s, j, d] == chunks[p][b, s, r * (H // P) + j, d]
+
+
+def pin_relayout_identity_and_round_trip():
+    """P = 1 is a plain copy; sending every rank its head slice and gathering
+    back gives the input bit for bit (NaN payloads included)."""
+    B, S_loc, H, D = 1, 5, 12, 8
+    x = synth.random_bits16((B, S_loc, H, D), 200)
+    assert np.array_equal(ref.relayout_seq_to_head([x], 1, 0), x)
+    for P in (2, 3, 4, 6):
+        chunks = [synth.random_bits16((B, S_loc, H, D), 300 + 10 * P + p) for p in range(P)]
+        ys = [ref.relayout_seq_to_head(chunks, P, r) for r in range(P)]
+        for p in range(P):
+            back = ref.relayout_head_to_seq(ys, P, p)
+            assert np.array_equal(back, chunks[p])
+
+
+def pin_relayout_head_limit():
+    """Ulysses degree must divide the head count: with 40 heads on 72 GPUs the
+    largest usable degree is 8 (the pages' example)."""
+    g = _golden()["ulysses_head_limit"]
+    H, G = g["num_heads"], g["gpus"]
+    ok = []
+    for P in range(1, H + 1):
+        chunks = [np.zeros((1, 2, H, 4), dtype=np.uint16)] * P
+        try:
+            ref.relayout_seq_to_head(chunks, P, 0)
+        except ValueError:
+            continue
+        if G % P == 0:
+            ok.append(P)
+    assert max(ok) == g["largest_ulysses_degree"]
+
+
+ATTENTION_PINS = [pin_identical_keys, pin_dominant_logit, pin_rows_sum_to_one, pin_single_key,
+                  pin_no_keys, pin_library_softmax, pin_brute_force_tiny,
+                  pin_permutation_and_scaling, pin_scale_argument]
+MERGE_PINS = [pin_merge_equals_full, pin_merge_attention2d_grid, pin_merge_closed_forms,
+              pin_ring_streaming_merge]
+RELAYOUT_PINS = [pin_relayout_index_map, pin_relayout_identity_and_round_trip, pin_relayout_head_limit]
+ALL_PINS = ATTENTION_PINS + MERGE_PINS + RELAYOUT_PINS

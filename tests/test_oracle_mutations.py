@@ -1,0 +1,165 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that the pins
+catch every one of them: a pin set that a dropped term, a wrong sign, a wrong
+index or a transposed operand slips through would not pin anything."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ref
+import oracle_pins as pins
+
+
+def _run(pin_list):
+    failed = []
+    for pin in pin_list:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    return failed
+
+
+def _block_no_scale(qh, kh, vh, scale):
+    return _orig_block(qh, kh, vh, 1.0)
+
+
+def _block_sqrt_mult(qh, kh, vh, scale):
+    return _orig_block(qh, kh, vh, 1.0 / scale)
+
+
+def _block_log2(qh, kh, vh, scale):
+    o, lse = _orig_block(qh, kh, vh, scale)
+    return o, lse / math.log(2.0)
+
+
+def _block_dropped_max(qh, kh, vh, scale):
+    s = (qh @ kh.T) * scale
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return (e @ vh) / l[:, None], np.log(l)
+
+
+def _block_no_normalise(qh, kh, vh, scale):
+    s = (qh @ kh.T) * scale
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    return e @ vh, m + np.log(e.sum(axis=1))
+
+
+def _block_wrong_sign(qh, kh, vh, scale):
+    return _orig_block(-qh, kh, vh, scale)
+
+
+def _block_transposed(qh, kh, vh, scale):
+    # keys and queries swapped: weights of key j over queries
+    s = (kh @ qh.T) * scale                      # [S_kv, n]
+    m = s.max(axis=0)
+    e = np.exp(s - m[None, :])
+    l = e.sum(axis=0)
+    w = (e / l[None, :]).T                       # still [n, S_kv] but normalised the wrong way
+    return w @ vh, m + np.log(l)
+
+
+def _block_off_by_one_key(qh, kh, vh, scale):
+    return _orig_block(qh, kh[:-1], vh[:-1], scale) if kh.shape[0] > 1 else _orig_block(qh, kh, vh, scale)
+
+
+def _block_v_shift(qh, kh, vh, scale):
+    return _orig_block(qh, kh, np.roll(vh, 1, axis=0), scale)
+
+
+_orig_block = ref._attend_block
+
+ATTN_MUTANTS = [_block_no_scale, _block_sqrt_mult, _block_log2, _block_dropped_max,
+                _block_no_normalise, _block_wrong_sign, _block_transposed,
+                _block_off_by_one_key, _block_v_shift]
+
+
+@pytest.mark.parametrize("mutant", ATTN_MUTANTS, ids=lambda f: f.__name__)
+def test_attention_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "_attend_block", mutant)
+    assert _run(pins.ATTENTION_PINS), f"{mutant.__name__} passed every attention pin"
+
+
+_orig_merge = ref.merge
+
+
+def _merge_unnormalised(o_parts, lse_parts):
+    O, L = _orig_merge(o_parts, lse_parts)
+    n = len(o_parts)
+    return O * n, L
+
+
+def _merge_dropped_max(o_parts, lse_parts):
+    O, L = _orig_merge(o_parts, lse_parts)
+    M = np.max(np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts]), axis=0)
+    with np.errstate(invalid="ignore"):
+        return O, np.where(np.isneginf(M), L, L - M)
+
+
+def _merge_wrong_sign(o_parts, lse_parts):
+    return _orig_merge(o_parts, [-np.asarray(x, dtype=np.float64) for x in lse_parts])
+
+
+def _merge_untransposed(o_parts, lse_parts):
+    # weights indexed [B, H, S] applied as if they were [B, S, H]
+    L = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])
+    M = L.max(axis=0)
+    w = np.exp(L - np.where(np.isneginf(M), 0.0, M)[None])
+    ws = w.sum(axis=0)
+    O = sum(np.reshape(w[i], (w.shape[1], w.shape[3], w.shape[2]))[..., None] * ref._as_f64(o)
+            for i, o in enumerate(o_parts))
+    O = O / np.reshape(ws, (ws.shape[0], ws.shape[2], ws.shape[1]))[..., None]
+    return O, M + np.log(ws)
+
+
+def _merge_first_only(o_parts, lse_parts):
+    return ref._as_f64(o_parts[0]), np.asarray(lse_parts[0], dtype=np.float64)
+
+
+MERGE_MUTANTS = [_merge_unnormalised, _merge_dropped_max, _merge_wrong_sign,
+                 _merge_untransposed, _merge_first_only]
+
+
+@pytest.mark.parametrize("mutant", MERGE_MUTANTS, ids=lambda f: f.__name__)
+def test_merge_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "merge", mutant)
+    assert _run(pins.MERGE_PINS), f"{mutant.__name__} passed every merge pin"
+
+
+_orig_relayout = ref.relayout_seq_to_head
+
+
+def _relayout_next_rank(chunks, P, rank):
+    return _orig_relayout(chunks, P, (rank + 1) % P)
+
+
+def _relayout_reversed_chunks(chunks, P, rank):
+    return _orig_relayout(list(chunks)[::-1], P, rank)
+
+
+def _relayout_no_check(chunks, P, rank):
+    B, S_loc, H, D = chunks[0].shape
+    hl = max(1, H // P)
+    return np.concatenate([c[:, :, rank * hl:(rank + 1) * hl, :] for c in chunks], axis=1)
+
+
+def _relayout_interleaved(chunks, P, rank):
+    y = _orig_relayout(chunks, P, rank)
+    B, S, hl, D = y.shape
+    S_loc = S // P
+    # tokens interleaved across shards instead of concatenated
+    return y.reshape(B, P, S_loc, hl, D).transpose(0, 2, 1, 3, 4).reshape(B, S, hl, D)
+
+
+RELAYOUT_MUTANTS = [_relayout_next_rank, _relayout_reversed_chunks, _relayout_no_check,
+                    _relayout_interleaved]
+
+
+@pytest.mark.parametrize("mutant", RELAYOUT_MUTANTS, ids=lambda f: f.__name__)
+def test_relayout_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "relayout_seq_to_head", mutant)
+    assert _run(pins.RELAYOUT_PINS), f"{mutant.__name__} passed every relayout pin"
