@@ -1,0 +1,142 @@
+/*
+ * lsd.h - C ABI of the long-sequence DiT attention library (MI355X, gfx950).
+ *
+ * Three calls make up the hot path of one sequence-parallel DiT attention
+ * layer on one GPU:
+ *
+ *   lsd_relayout_seq_to_head  seq-major shards -> head-major slice (Ulysses)
+ *   lsd_attn_fwd              dense bidirectional attention, O and optional LSE
+ *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - A tensor is described by an lsd_view4: a device pointer to element
+ *   [0,0,0,0] plus a logical 4-d shape and strides counted in ELEMENTS.  The
+ *   logical order is (B, S, H, D): batch, sequence, head, head channel.
+ *   stride[3] must be 1 (head channels contiguous); the other strides are
+ *   free (non-negative), so strided views such as Q, K or V inside a fused
+ *   QKV projection buffer [B, S, 3, H, D] are accepted without a copy.
+ * - Elements of lsd_view4 tensors are bfloat16 (16-bit) unless stated.  LSE
+ *   arrays are float32, laid out [B, H, S] contiguous.
+ * - Alignment: every view's data pointer and strides[0..2] must give 16-byte
+ *   aligned rows (pointer % 16 == 0, stride % 8 == 0 elements, D % 8 == 0).
+ * - Ownership: the caller allocates and frees all device memory.  The library
+ *   allocates nothing, keeps no pointer after a call returns, and never
+ *   synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) in call order.
+ * - Errors: arguments are validated on the host before any HIP call; a
+ *   violation returns LSD_EINVAL (bad argument) or LSD_EUNSUPPORTED (valid
+ *   request outside what the kernels implement) and nothing is enqueued.  A
+ *   launch failure returns LSD_EDEVICE.  Faults inside a kernel surface at the
+ *   caller's next synchronisation, as with any HIP call.  There is no
+ *   fallback path: an unsupported request always fails loudly.
+ *   lsd_last_error() returns a thread-local message for the last failure.
+ * - Outputs may not overlap inputs (checked by address range): LSD_EINVAL.
+ * - Results are deterministic: fixed reduction order, no atomics.
+ */
+#ifndef LSD_H
+#define LSD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSD_ABI_VERSION 1
+
+typedef enum lsd_status {
+  LSD_OK = 0,
+  LSD_EINVAL = 1,
+  LSD_EUNSUPPORTED = 2,
+  LSD_EDEVICE = 3
+} lsd_status;
+
+typedef struct lsd_view4 {
+  void* data;        /* device pointer to element [0,0,0,0] */
+  int64_t shape[4];  /* (B, S, H, D) */
+  int64_t stride[4]; /* element strides; stride[3] == 1 */
+} lsd_view4;
+
+/* LSD_ABI_VERSION of the built library. */
+int lsd_abi_version(void);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* lsd_last_error(void);
+
+/*
+ * Dense, unmasked, bidirectional multi-head attention with log-sum-exp.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM":
+ * "The Scaling Challenge in Video Generation" (every denoising step attends
+ * over the whole sequence, no causal mask) and "Context Parallelism >
+ * Attention2D Parallelism > Local Attention" (the inner backend returns the
+ * partial output [B, S_q, H, D] and the LSE [B, H, S_q] of its pass).
+ *
+ *   q   (B, S_q,  H, D) bf16        k, v (B, S_kv, H, D) bf16
+ *   o   (B, S_q,  H, D) bf16, written
+ *   lse float32 [B, H, S_q] contiguous, written if non-NULL
+ *
+ * For each (b, h, i):  s_ij = scale * q_i . k_j,
+ *   LSE_i = ln sum_j exp(s_ij)   (natural log of the scaled logits),
+ *   O_i   = sum_j exp(s_ij - LSE_i) v_j, rounded to bf16 (nearest-even).
+ * S_q and S_kv may differ (a query block against a key/value block).
+ * S_kv == 0 gives O = 0 and LSE = -inf.  Zero-sized B, S_q or H is a no-op.
+ * softmax_scale <= 0 (or NaN) selects 1/sqrt(D); +inf is rejected.
+ * D must be 64 or 128 (LSD_EUNSUPPORTED otherwise).  The device must be
+ * gfx950 (LSD_EUNSUPPORTED otherwise).
+ */
+lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
+                        const lsd_view4* o, float* lse, float softmax_scale, void* stream);
+
+/*
+ * Exact merge of n partial attention results over disjoint key spans.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+ * "Context Parallelism > Ring Attention" (online-softmax merge of per-block
+ * outputs and LSE) and "Attention2D Parallelism > Merge phase" (one batched
+ * combine of the received (output, LSE) pairs).
+ *
+ *   o_parts[i]   (B, S, H, D) bf16, i = 0..n-1 (any strides as above)
+ *   lse_parts[i] float32 [B, H, S] contiguous
+ *   o_out        (B, S, H, D) bf16, written
+ *   lse_out      float32 [B, H, S] contiguous, written if non-NULL
+ *
+ * With M = max_i LSE_i and w_i = exp(LSE_i - M):
+ *   LSE = M + ln sum_i w_i,   O = (sum_i w_i O_i) / sum_i w_i  (float32 math,
+ *   partials summed in order i = 0..n-1, O rounded to bf16 nearest-even).
+ * Where every LSE_i is -inf: O = 0, LSE = -inf.  1 <= n <= 16.
+ * o_out and lse_out may not overlap any input.
+ */
+lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* lse_parts,
+                          const lsd_view4* o_out, float* lse_out, void* stream);
+
+/*
+ * Ulysses sequence-major -> head-major relayout for one destination rank.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+ * "Ulysses Parallelism" ([B, S/P, H, D] -> [B, S, H/P, D]; P must divide H;
+ * the fused variant moves Q, K and V together), and by "CUDA IPC Ulysses"
+ * (TeleFuser), sections "Baseline and bottleneck" and "Strided Copy Engine
+ * scatter" (the fused projection's V is read as a strided view, each token's
+ * heads and channels contiguous, written straight into the final
+ * (B, S_global, H_local, D) layout).
+ *
+ *   src  n_tensors * P views, index t*P + p: sequence shard p of tensor t,
+ *        each (B, S_loc, H, D); all of one shape.
+ *   dst  n_tensors views, each (B, P*S_loc, H/P, D), written.
+ *
+ *   dst[t][b, p*S_loc + s, j, :] = src[t*P + p][b, s, rank*(H/P) + j, :]
+ *
+ * A pure 16-bit copy: every bit pattern (NaN payloads, -0) is preserved.
+ * 1 <= n_tensors <= 3, 1 <= P <= 16, 0 <= rank < P, H % P == 0 (LSD_EINVAL
+ * otherwise).  Destinations may not overlap any source or each other.
+ */
+lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src,
+                                    const lsd_view4* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSD_H */

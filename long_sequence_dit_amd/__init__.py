@@ -1,0 +1,173 @@
+"""Python binding of liblsd.so, the MI355X long-sequence DiT attention library.
+
+Argument marshalling only: each function turns torch tensors (device memory
+and the current stream) into the C-ABI views of ``include/lsd.h`` and calls
+the matching entry point; every step of the computation runs in the HIP
+kernels.  There is no fallback: if the library is missing, or a tensor is not
+on a GPU, or the device is not gfx950, the call raises.
+
+Entry points (same names as the C ABI without the ``lsd_`` prefix):
+
+* ``attn_fwd(q, k, v, o=None, lse=None, scale=None, return_lse=True)``
+* ``attn_merge(o_parts, lse_parts, o=None, lse=None, return_lse=True)``
+* ``relayout_seq_to_head(src, P, rank, dst=None)``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsd.so")
+
+LSD_OK, LSD_EINVAL, LSD_EUNSUPPORTED, LSD_EDEVICE = 0, 1, 2, 3
+
+
+class View4(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p),
+                ("shape", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liblsd.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m long_sequence_dit_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.lsd_abi_version.restype = ctypes.c_int
+        L.lsd_last_error.restype = ctypes.c_char_p
+        L.lsd_attn_fwd.restype = ctypes.c_int
+        L.lsd_attn_fwd.argtypes = [P(View4), P(View4), P(View4), P(View4), ctypes.c_void_p,
+                                   ctypes.c_float, ctypes.c_void_p]
+        L.lsd_attn_merge.restype = ctypes.c_int
+        L.lsd_attn_merge.argtypes = [ctypes.c_int, P(View4), P(ctypes.c_void_p), P(View4),
+                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.lsd_relayout_seq_to_head.restype = ctypes.c_int
+        L.lsd_relayout_seq_to_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
+                                               P(View4), ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == LSD_OK:
+        return
+    msg = lib().lsd_last_error().decode(errors="replace")
+    if status in (LSD_EINVAL, LSD_EUNSUPPORTED):
+        raise ValueError(f"{what}: {msg}")
+    raise RuntimeError(f"{what}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+_16BIT = None
+
+
+def _view(t, name: str) -> View4:
+    torch = _torch()
+    global _16BIT
+    if _16BIT is None:
+        _16BIT = {torch.bfloat16, torch.int16, torch.uint16, torch.float16}
+    if t.dim() != 4:
+        raise ValueError(f"{name}: expected a 4-d (B, S, H, D) tensor, got {t.dim()}-d")
+    if t.dtype not in _16BIT:
+        raise ValueError(f"{name}: expected 16-bit elements (bfloat16), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must be in GPU memory (HIP library, no CPU path)")
+    v = View4()
+    v.data = t.data_ptr()
+    for i in range(4):
+        v.shape[i] = t.shape[i]
+        v.stride[i] = t.stride(i)
+    return v
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _f32_ptr(t, name, shape):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous float32 GPU tensor of shape {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_lse: bool = True):
+    """O = softmax(scale * Q K^T) V per (batch, head), plus the natural-log LSE.
+
+    q: (B, S_q, H, D) bf16, k/v: (B, S_kv, H, D) bf16 (strided views allowed,
+    last dim contiguous).  Returns ``o`` (and ``lse`` [B, H, S_q] float32 when
+    ``return_lse``).  ``scale`` defaults to 1/sqrt(D).
+    """
+    torch = _torch()
+    B, S_q, H, D = q.shape
+    if o is None:
+        o = torch.empty((B, S_q, H, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    vq, vk, vv, vo = _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o")
+    lp = _f32_ptr(lse, "lse", (B, H, S_q)) if lse is not None else None
+    st = lib().lsd_attn_fwd(ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), ctypes.byref(vo), lp,
+                            ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q))
+    _check(st, "lsd_attn_fwd")
+    return (o, lse) if lse is not None else o
+
+
+def attn_merge(o_parts: Sequence, lse_parts: Sequence, o=None, lse=None, return_lse: bool = True):
+    """Exact log-sum-exp merge of n partial (O_i, LSE_i) over disjoint key spans."""
+    torch = _torch()
+    n = len(o_parts)
+    if n != len(lse_parts) or n == 0:
+        raise ValueError("attn_merge: need as many LSE arrays as partial outputs (n >= 1)")
+    B, S, H, D = o_parts[0].shape
+    if o is None:
+        o = torch.empty((B, S, H, D), dtype=o_parts[0].dtype, device=o_parts[0].device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o.device)
+    views = (View4 * n)(*[_view(t, f"o_parts[{i}]") for i, t in enumerate(o_parts)])
+    ptrs = (ctypes.c_void_p * n)(*[_f32_ptr(t, f"lse_parts[{i}]", (B, H, S)).value
+                                   for i, t in enumerate(lse_parts)])
+    vo = _view(o, "o")
+    lp = _f32_ptr(lse, "lse", (B, H, S)) if lse is not None else None
+    st = lib().lsd_attn_merge(n, views, ptrs, ctypes.byref(vo), lp, _stream(o))
+    _check(st, "lsd_attn_merge")
+    return (o, lse) if lse is not None else o
+
+
+def relayout_seq_to_head(src: Sequence[Sequence], P: int, rank: int, dst: Optional[List] = None):
+    """Ulysses seq-major -> head-major relayout for destination ``rank``.
+
+    src: one list per tensor (1 to 3 of them, e.g. Q, K, V), each holding the P
+    sequence shards (B, S_loc, H, D).  Returns one (B, P*S_loc, H/P, D) tensor
+    per source tensor.
+    """
+    torch = _torch()
+    nt = len(src)
+    if nt == 0 or any(len(s) != P for s in src):
+        raise ValueError("relayout_seq_to_head: src must be n_tensors lists of P shards each")
+    B, S_loc, H, D = src[0][0].shape
+    if dst is None:
+        if H % P != 0:
+            raise ValueError(f"relayout_seq_to_head: head count H={H} is not divisible by P={P}")
+        dst = [torch.empty((B, P * S_loc, H // P, D), dtype=src[0][0].dtype, device=src[0][0].device)
+               for _ in range(nt)]
+    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{p}]") for t, s in enumerate(src) for p, c in enumerate(s)])
+    dv = (View4 * nt)(*[_view(d, f"dst[{t}]") for t, d in enumerate(dst)])
+    st = lib().lsd_relayout_seq_to_head(nt, P, rank, sv, dv, _stream(src[0][0]))
+    _check(st, "lsd_relayout_seq_to_head")
+    return dst

@@ -1,0 +1,286 @@
+// C-ABI entry points: host-side argument validation, then one kernel launch.
+// Every check runs before any HIP call, so a rejected request enqueues nothing
+// and touches no device state.  See include/lsd.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "lsd.h"
+#include "lsd_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lsd_status fail(lsd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+lsd_status ok() {
+  g_err.clear();
+  return LSD_OK;
+}
+
+bool view_empty(const lsd_view4& v) {
+  for (int i = 0; i < 4; ++i)
+    if (v.shape[i] == 0) return true;
+  return false;
+}
+
+// Byte range [lo, hi) touched by a view of elements of `eb` bytes.
+struct Span {
+  uintptr_t lo = 0, hi = 0;
+};
+
+Span span_of(const lsd_view4& v, int eb) {
+  Span s;
+  if (view_empty(v)) return s;
+  int64_t last = 0;
+  for (int i = 0; i < 4; ++i) last += (v.shape[i] - 1) * v.stride[i];
+  s.lo = (uintptr_t)v.data;
+  s.hi = s.lo + (uintptr_t)(last + 1) * (uintptr_t)eb;
+  return s;
+}
+
+Span span_flat(const void* p, int64_t n, int eb) {
+  Span s;
+  if (p == nullptr || n <= 0) return s;
+  s.lo = (uintptr_t)p;
+  s.hi = s.lo + (uintptr_t)n * (uintptr_t)eb;
+  return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Structural checks shared by every bf16 view.
+lsd_status check_view(const char* name, const lsd_view4* v) {
+  if (v == nullptr) return fail(LSD_EINVAL, "%s: null view", name);
+  for (int i = 0; i < 4; ++i) {
+    if (v->shape[i] < 0) return fail(LSD_EINVAL, "%s: negative shape[%d]", name, i);
+    if (v->shape[i] > 0x7fffffff) return fail(LSD_EINVAL, "%s: shape[%d] exceeds 2^31-1", name, i);
+    if (v->stride[i] < 0) return fail(LSD_EINVAL, "%s: negative stride[%d]", name, i);
+  }
+  if (view_empty(*v)) return LSD_OK;
+  if (v->data == nullptr) return fail(LSD_EINVAL, "%s: null data pointer", name);
+  if (v->stride[3] != 1 && v->shape[3] > 1)
+    return fail(LSD_EINVAL, "%s: stride[3] must be 1 (head channels contiguous)", name);
+  if ((uintptr_t)v->data % 16 != 0) return fail(LSD_EINVAL, "%s: data pointer not 16-byte aligned", name);
+  if (v->shape[3] % 8 != 0) return fail(LSD_EINVAL, "%s: D=%lld is not a multiple of 8", name, (long long)v->shape[3]);
+  for (int i = 0; i < 3; ++i)
+    if (v->shape[i] > 1 && v->stride[i] % 8 != 0)
+      return fail(LSD_EINVAL, "%s: stride[%d]=%lld is not a multiple of 8 elements (16 bytes)", name, i,
+                  (long long)v->stride[i]);
+  // the largest element offset must fit comfortably in 64-bit byte arithmetic
+  double last = 0;
+  for (int i = 0; i < 4; ++i) last += (double)(v->shape[i] - 1) * (double)v->stride[i];
+  if (last * 2.0 > 9.0e18) return fail(LSD_EINVAL, "%s: view spans more than 2^62 bytes", name);
+  return LSD_OK;
+}
+
+bool same_shape(const lsd_view4& a, const lsd_view4& b) {
+  for (int i = 0; i < 4; ++i)
+    if (a.shape[i] != b.shape[i]) return false;
+  return true;
+}
+
+std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+lsd_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LSD_EDEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(LSD_EDEVICE, "device index %d out of range", dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(LSD_EDEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(LSD_EUNSUPPORTED, "device %d is not gfx950 (MI355X); the kernels are built for gfx950 only", dev);
+  return LSD_OK;
+}
+
+lsd_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LSD_EDEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int lsd_abi_version(void) { return LSD_ABI_VERSION; }
+
+const char* lsd_last_error(void) { return g_err.c_str(); }
+
+lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const lsd_view4* o,
+                        float* lse, float softmax_scale, void* stream) {
+  lsd_status s;
+  if ((s = check_view("q", q)) != LSD_OK) return s;
+  if ((s = check_view("k", k)) != LSD_OK) return s;
+  if ((s = check_view("v", v)) != LSD_OK) return s;
+  if ((s = check_view("o", o)) != LSD_OK) return s;
+  const int64_t B = q->shape[0], S_q = q->shape[1], H = q->shape[2], D = q->shape[3];
+  const int64_t S_kv = k->shape[1];
+  if (k->shape[0] != B || k->shape[2] != H || k->shape[3] != D)
+    return fail(LSD_EINVAL, "k shape (%lld,%lld,%lld,%lld) does not match q (B=%lld, H=%lld, D=%lld)",
+                (long long)k->shape[0], (long long)k->shape[1], (long long)k->shape[2], (long long)k->shape[3],
+                (long long)B, (long long)H, (long long)D);
+  if (!same_shape(*v, *k)) return fail(LSD_EINVAL, "v shape must equal k shape (B, S_kv, H, D)");
+  if (!same_shape(*o, *q)) return fail(LSD_EINVAL, "o shape must equal q shape (B, S_q, H, D)");
+  if (D != 64 && D != 128) return fail(LSD_EUNSUPPORTED, "head dim D=%lld unsupported (64 or 128)", (long long)D);
+  if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
+  if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
+  if (B * S_q * H == 0) return ok();
+
+  const Span so = span_of(*o, 2);
+  const Span sl = span_flat(lse, B * H * S_q, 4);
+  const Span sq = span_of(*q, 2), sk = span_of(*k, 2), sv = span_of(*v, 2);
+  if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv))
+    return fail(LSD_EINVAL, "o overlaps an input (q, k or v)");
+  if (overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv) || overlaps(sl, so))
+    return fail(LSD_EINVAL, "lse overlaps o or an input");
+  if ((s = check_device()) != LSD_OK) return s;
+
+  const float scale = (softmax_scale > 0.0f) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  lsd::AttnArgs a;
+  a.q = (const uint16_t*)q->data;
+  a.k = (const uint16_t*)k->data;
+  a.v = (const uint16_t*)v->data;
+  a.o = (uint16_t*)o->data;
+  a.lse = lse;
+  a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
+  a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2];
+  a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv; a.D = (int)D;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd");
+}
+
+lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* lse_parts, const lsd_view4* o_out,
+                          float* lse_out, void* stream) {
+  if (n < 1) return fail(LSD_EINVAL, "n=%d: need at least one partial", n);
+  if (n > lsd::kMaxMerge) return fail(LSD_EUNSUPPORTED, "n=%d partials: at most %d per call", n, lsd::kMaxMerge);
+  if (o_parts == nullptr || lse_parts == nullptr) return fail(LSD_EINVAL, "null o_parts or lse_parts array");
+  lsd_status s;
+  if ((s = check_view("o_out", o_out)) != LSD_OK) return s;
+  char name[32];
+  for (int i = 0; i < n; ++i) {
+    std::snprintf(name, sizeof name, "o_parts[%d]", i);
+    if ((s = check_view(name, &o_parts[i])) != LSD_OK) return s;
+    if (!same_shape(o_parts[i], *o_out)) return fail(LSD_EINVAL, "o_parts[%d] shape differs from o_out", i);
+  }
+  const int64_t B = o_out->shape[0], S = o_out->shape[1], H = o_out->shape[2], D = o_out->shape[3];
+  if (D > 8 * 256) return fail(LSD_EUNSUPPORTED, "D=%lld too large for the merge kernel (<= 2048)", (long long)D);
+  if (lse_out != nullptr && (uintptr_t)lse_out % 4 != 0) return fail(LSD_EINVAL, "lse_out not 4-byte aligned");
+  if (B * S * H * D == 0) return ok();
+  for (int i = 0; i < n; ++i) {
+    if (lse_parts[i] == nullptr) return fail(LSD_EINVAL, "lse_parts[%d] is null", i);
+    if ((uintptr_t)lse_parts[i] % 4 != 0) return fail(LSD_EINVAL, "lse_parts[%d] not 4-byte aligned", i);
+  }
+  const Span so = span_of(*o_out, 2);
+  const Span slo = span_flat(lse_out, B * H * S, 4);
+  if (overlaps(so, slo)) return fail(LSD_EINVAL, "o_out overlaps lse_out");
+  for (int i = 0; i < n; ++i) {
+    const Span si = span_of(o_parts[i], 2), sli = span_flat(lse_parts[i], B * H * S, 4);
+    if (overlaps(so, si) || overlaps(so, sli)) return fail(LSD_EINVAL, "o_out overlaps partial %d", i);
+    if (overlaps(slo, si) || overlaps(slo, sli)) return fail(LSD_EINVAL, "lse_out overlaps partial %d", i);
+  }
+  if ((s = check_device()) != LSD_OK) return s;
+
+  lsd::MergeArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int i = 0; i < n; ++i) {
+    a.o_in[i] = (const uint16_t*)o_parts[i].data;
+    a.in_sb[i] = o_parts[i].stride[0];
+    a.in_ss[i] = o_parts[i].stride[1];
+    a.in_sh[i] = o_parts[i].stride[2];
+    a.lse_in[i] = lse_parts[i];
+  }
+  a.o_out = (uint16_t*)o_out->data;
+  a.out_sb = o_out->stride[0]; a.out_ss = o_out->stride[1]; a.out_sh = o_out->stride[2];
+  a.lse_out = lse_out;
+  a.n = n; a.B = (int)B; a.S = (int)S; a.H = (int)H; a.D = (int)D;
+  return launched(lsd::launch_attn_merge(a, (hipStream_t)stream), "attn_merge");
+}
+
+lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,
+                                    void* stream) {
+  if (n_tensors < 1 || n_tensors > lsd::kMaxRelayoutTensors)
+    return fail(LSD_EINVAL, "n_tensors=%d: must be 1..%d (Q, K, V)", n_tensors, lsd::kMaxRelayoutTensors);
+  if (P < 1) return fail(LSD_EINVAL, "P=%d: sequence-parallel degree must be >= 1", P);
+  if (P > lsd::kMaxRelayoutP) return fail(LSD_EUNSUPPORTED, "P=%d: at most %d shards per call", P, lsd::kMaxRelayoutP);
+  if (rank < 0 || rank >= P) return fail(LSD_EINVAL, "rank=%d not in [0, P=%d)", rank, P);
+  if (src == nullptr || dst == nullptr) return fail(LSD_EINVAL, "null src or dst array");
+  lsd_status s;
+  char name[48];
+  for (int i = 0; i < n_tensors * P; ++i) {
+    std::snprintf(name, sizeof name, "src[%d] (tensor %d, shard %d)", i, i / P, i % P);
+    if ((s = check_view(name, &src[i])) != LSD_OK) return s;
+    if (!same_shape(src[i], src[0]))
+      return fail(LSD_EINVAL, "src[%d]: sequence shards must all have the same shape (B, S_loc, H, D)", i);
+  }
+  const int64_t B = src[0].shape[0], S_loc = src[0].shape[1], H = src[0].shape[2], D = src[0].shape[3];
+  if (H % P != 0) return fail(LSD_EINVAL, "head count H=%lld is not divisible by P=%d", (long long)H, P);
+  const int64_t H_loc = H / P;
+  if ((int64_t)P * S_loc > 0x7fffffff) return fail(LSD_EINVAL, "P*S_loc exceeds 2^31-1");
+  for (int t = 0; t < n_tensors; ++t) {
+    std::snprintf(name, sizeof name, "dst[%d]", t);
+    if ((s = check_view(name, &dst[t])) != LSD_OK) return s;
+    const lsd_view4& d = dst[t];
+    if (d.shape[0] != B || d.shape[1] != P * S_loc || d.shape[2] != H_loc || d.shape[3] != D)
+      return fail(LSD_EINVAL, "dst[%d] shape must be (B=%lld, P*S_loc=%lld, H/P=%lld, D=%lld)", t, (long long)B,
+                  (long long)(P * S_loc), (long long)H_loc, (long long)D);
+  }
+  if (B * S_loc * H_loc * D == 0) return ok();
+  for (int t = 0; t < n_tensors; ++t) {
+    const Span sd = span_of(dst[t], 2);
+    for (int i = 0; i < n_tensors * P; ++i)
+      if (overlaps(sd, span_of(src[i], 2))) return fail(LSD_EINVAL, "dst[%d] overlaps src[%d]", t, i);
+    for (int u = 0; u < t; ++u)
+      if (overlaps(sd, span_of(dst[u], 2))) return fail(LSD_EINVAL, "dst[%d] overlaps dst[%d]", t, u);
+  }
+  if ((s = check_device()) != LSD_OK) return s;
+
+  lsd::RelayoutArgs a;
+  std::memset(&a, 0, sizeof a);
+  bool contiguous_heads = true;
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int p = 0; p < P; ++p) {
+      const lsd_view4& v = src[t * P + p];
+      a.src[t][p] = (const uint16_t*)v.data;
+      a.src_sb[t][p] = v.stride[0];
+      a.src_ss[t][p] = v.stride[1];
+      a.src_sh[t][p] = v.stride[2];
+      if (H_loc > 1 && v.stride[2] != D) contiguous_heads = false;
+    }
+    a.dst[t] = (uint16_t*)dst[t].data;
+    a.dst_sb[t] = dst[t].stride[0];
+    a.dst_ss[t] = dst[t].stride[1];
+    a.dst_sh[t] = dst[t].stride[2];
+    if (H_loc > 1 && dst[t].stride[2] != D) contiguous_heads = false;
+  }
+  a.n_tensors = n_tensors; a.P = P; a.rank = rank; a.B = (int)B; a.S_loc = (int)S_loc;
+  a.H_loc = (int)H_loc; a.D = (int)D;
+  a.heads_per_run = contiguous_heads ? (int)H_loc : 1;
+  return launched(lsd::launch_relayout(a, (hipStream_t)stream), "relayout_seq_to_head");
+}
+
+}  // extern "C"

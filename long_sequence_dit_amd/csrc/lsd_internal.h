@@ -1,0 +1,54 @@
+// Internal launch interface between the C-ABI validation layer (api.cpp) and
+// the HIP kernels.  Not installed; the public interface is include/lsd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsd {
+
+// Attention forward.  Strides are in elements; D (head channels) contiguous.
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // [B, H, S_q] contiguous, may be null
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int B, H, S_q, S_kv, D;
+  float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+
+constexpr int kMaxMerge = 16;
+
+struct MergeArgs {
+  const uint16_t* o_in[kMaxMerge];
+  int64_t in_sb[kMaxMerge], in_ss[kMaxMerge], in_sh[kMaxMerge];
+  const float* lse_in[kMaxMerge];
+  uint16_t* o_out;
+  int64_t out_sb, out_ss, out_sh;
+  float* lse_out;  // may be null
+  int n, B, S, H, D;
+};
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream);
+
+constexpr int kMaxRelayoutTensors = 3;
+constexpr int kMaxRelayoutP = 16;
+
+struct RelayoutArgs {
+  const uint16_t* src[kMaxRelayoutTensors][kMaxRelayoutP];
+  int64_t src_sb[kMaxRelayoutTensors][kMaxRelayoutP];
+  int64_t src_ss[kMaxRelayoutTensors][kMaxRelayoutP];
+  int64_t src_sh[kMaxRelayoutTensors][kMaxRelayoutP];
+  uint16_t* dst[kMaxRelayoutTensors];
+  int64_t dst_sb[kMaxRelayoutTensors], dst_ss[kMaxRelayoutTensors], dst_sh[kMaxRelayoutTensors];
+  int n_tensors, P, rank, B, S_loc, H_loc, D;
+  int heads_per_run;  // H_loc when every head slice is contiguous in src and dst, else 1
+};
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream);
+
+}  // namespace lsd

@@ -1,0 +1,83 @@
+// Ulysses sequence-major -> head-major relayout for one destination rank, gfx950.
+//
+//   dst[t][b, p*S_loc + s, j, :] = src[t][p][b, s, rank*H_loc + j, :]
+//
+// ("Scaling Video Generation Across NVL72 rack with TensorRT-LLM", "Ulysses
+// Parallelism": [B, S/P, H, D] -> [B, S, H/P, D], Q/K/V moved together from the
+// fused projection; "CUDA IPC Ulysses" (TeleFuser), "Strided Copy Engine
+// scatter": the strided V view is read in place and written straight into the
+// final layout.)  A pure copy of 16-bit patterns; no arithmetic.
+//
+// HBM-bound stream.  The copy is cut into runs: one run is the H_loc*D
+// contiguous elements one token contributes to one tensor (or one head's D
+// elements when a view's head slices are not contiguous).  Each wave copies
+// whole runs with 16-byte loads and stores; all loads of a run are issued
+// before its stores.  Run indices are wave-uniform, so the per-run address
+// arithmetic (tensor, shard, token) stays in scalar registers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsd_internal.h"
+
+namespace lsd {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kUnroll = 4;  // 16-byte vectors per lane in flight per pass
+
+__global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a, int64_t n_runs) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = a.P * a.S_loc;
+  const int runs_per_token = a.H_loc / a.heads_per_run;
+  const int vpr = a.heads_per_run * a.D / 8;  // vectors per run
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+
+  for (int64_t run = (int64_t)blockIdx.x * kWavesPerBlock + wave; run < n_runs; run += stride) {
+    const int jr = (int)(run % runs_per_token);
+    const int64_t tok = run / runs_per_token;
+    const int sg = (int)(tok % S);
+    const int64_t tb = tok / S;
+    const int b = (int)(tb % a.B);
+    const int t = (int)(tb / a.B);
+    const int p = sg / a.S_loc;
+    const int s = sg - p * a.S_loc;
+    const int j0 = jr * a.heads_per_run;
+
+    const uint16_t* sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)s * a.src_ss[t][p] +
+                         (int64_t)(a.rank * a.H_loc + j0) * a.src_sh[t][p];
+    uint16_t* dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)sg * a.dst_ss[t] + (int64_t)j0 * a.dst_sh[t];
+
+    for (int v0 = 0; v0 < vpr; v0 += 64 * kUnroll) {
+      u32x4 buf[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < vpr) buf[u] = *(const u32x4*)(sp + 8 * v);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < vpr) *(u32x4*)(dp + 8 * v) = buf[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream) {
+  const int64_t n_runs = (int64_t)a.n_tensors * a.B * a.P * a.S_loc * (a.H_loc / a.heads_per_run);
+  if (n_runs == 0) return hipSuccess;
+  // enough waves to cover the chip several times; each wave loops over runs
+  int64_t blocks = (n_runs + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = 256 * 8 * 4;  // CUs x (workgroups per CU in flight) x passes
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, n_runs);
+  return hipGetLastError();
+}
+
+}  // namespace lsd

@@ -1,0 +1,183 @@
+"""The C-ABI library (CPU only): it loads, exports every entry point that
+include/lsd.h declares, and rejects invalid requests on the host before any
+HIP call.  Pointers here are fake (aligned addresses that are never
+dereferenced): validation is pure address arithmetic."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_sequence_dit_amd as lsd
+from long_sequence_dit_amd import View4, LSD_EINVAL, LSD_EUNSUPPORTED
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lsd.h")
+
+BASE = 1 << 40  # fake, 16-byte aligned device addresses
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = lsd.lib()
+    syms = declared_symbols()
+    assert {"lsd_attn_fwd", "lsd_attn_merge", "lsd_relayout_seq_to_head",
+            "lsd_abi_version", "lsd_last_error"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in lsd.h but not exported by liblsd.so"
+    assert L.lsd_abi_version() == 1
+
+
+def view(addr, shape, stride=None):
+    if stride is None:
+        stride = [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+    v = View4()
+    v.data = addr
+    for i in range(4):
+        v.shape[i] = shape[i]
+        v.stride[i] = stride[i]
+    return v
+
+
+def attn(q, k, v, o, lse=None, scale=0.0):
+    L = lsd.lib()
+    r = L.lsd_attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                       None if lse is None else ctypes.c_void_p(lse), ctypes.c_float(scale), None)
+    return r, L.lsd_last_error().decode()
+
+
+GB = 1 << 30
+
+
+def good4(S_q=256, S_kv=256, H=2, D=64, B=1):
+    return (view(BASE, (B, S_q, H, D)), view(BASE + GB, (B, S_kv, H, D)),
+            view(BASE + 2 * GB, (B, S_kv, H, D)), view(BASE + 3 * GB, (B, S_q, H, D)))
+
+
+@pytest.mark.parametrize("case,status,needle", [
+    ("D=96", LSD_EUNSUPPORTED, "head dim"),
+    ("k_heads", LSD_EINVAL, "does not match"),
+    ("v_shape", LSD_EINVAL, "v shape"),
+    ("o_shape", LSD_EINVAL, "o shape"),
+    ("stride3", LSD_EINVAL, "stride[3]"),
+    ("misaligned", LSD_EINVAL, "16-byte aligned"),
+    ("stride_align", LSD_EINVAL, "multiple of 8"),
+    ("null_data", LSD_EINVAL, "null data"),
+    ("negative", LSD_EINVAL, "negative"),
+    ("alias", LSD_EINVAL, "overlaps"),
+    ("lse_alias", LSD_EINVAL, "lse overlaps"),
+    ("inf_scale", LSD_EINVAL, "infinite"),
+])
+def test_attn_fwd_validation(case, status, needle):
+    q, k, v, o = good4()
+    lse = None
+    scale = 0.0
+    if case == "D=96":
+        q, k, v, o = good4(D=96)
+    elif case == "k_heads":
+        k = view(BASE + GB, (1, 256, 3, 64))
+    elif case == "v_shape":
+        v = view(BASE + 2 * GB, (1, 128, 2, 64))
+    elif case == "o_shape":
+        o = view(BASE + 3 * GB, (1, 255, 2, 64))
+    elif case == "stride3":
+        q = view(BASE, (1, 256, 2, 64), [256 * 128 * 2, 256, 128, 2])
+    elif case == "misaligned":
+        q = view(BASE + 8, (1, 256, 2, 64))
+    elif case == "stride_align":
+        q = view(BASE, (1, 256, 2, 64), [256 * 132, 132, 68, 1])
+    elif case == "null_data":
+        k = view(0, (1, 256, 2, 64))
+    elif case == "negative":
+        q = view(BASE, (1, 256, 2, 64), [-1, 128, 64, 1])
+    elif case == "alias":
+        o = view(BASE + 64, (1, 256, 2, 64))
+    elif case == "lse_alias":
+        lse = BASE + 3 * GB + 4096
+    elif case == "inf_scale":
+        scale = float("inf")
+    r, msg = attn(q, k, v, o, lse, scale)
+    assert r == status and needle in msg, (r, msg)
+
+
+def test_attn_fwd_zero_size_is_noop():
+    q, k, v, o = good4(S_q=0)
+    r, msg = attn(q, k, v, o)
+    assert r == 0 and msg == ""
+
+
+def merge(n, parts, lses, out, lse_out=None):
+    L = lsd.lib()
+    arr = (View4 * max(1, len(parts)))(*parts) if parts else None
+    ptrs = (ctypes.c_void_p * max(1, len(lses)))(*lses) if lses else None
+    r = L.lsd_attn_merge(n, arr, ptrs, ctypes.byref(out), None if lse_out is None else ctypes.c_void_p(lse_out),
+                         None)
+    return r, L.lsd_last_error().decode()
+
+
+def test_attn_merge_validation():
+    shp = (1, 100, 4, 128)
+    parts = [view(BASE + i * GB, shp) for i in range(3)]
+    lses = [BASE + (10 + i) * GB for i in range(3)]
+    out = view(BASE + 20 * GB, shp)
+    assert merge(0, parts, lses, out)[0] == LSD_EINVAL
+    assert merge(17, parts * 6, lses * 6, out)[0] == LSD_EUNSUPPORTED
+    bad = [parts[0], view(BASE + GB, (1, 99, 4, 128)), parts[2]]
+    r, msg = merge(3, bad, lses, out)
+    assert r == LSD_EINVAL and "shape differs" in msg
+    r, msg = merge(3, parts, [lses[0], 0, lses[2]], out)
+    assert r == LSD_EINVAL and "null" in msg
+    r, msg = merge(3, parts, lses, view(BASE + GB + 512, shp))
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = merge(3, parts, lses, out, lse_out=lses[1] + 64)
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = merge(3, parts, lses, out, lse_out=BASE + 30 * GB + 2)
+    assert r == LSD_EINVAL and "aligned" in msg
+
+
+def relayout(nt, P, rank, src, dst):
+    L = lsd.lib()
+    sv = (View4 * len(src))(*src)
+    dv = (View4 * len(dst))(*dst)
+    r = L.lsd_relayout_seq_to_head(nt, P, rank, sv, dv, None)
+    return r, L.lsd_last_error().decode()
+
+
+def test_relayout_validation():
+    B, S_loc, H, D, P = 2, 50, 40, 128, 4
+    fused = [S_loc * 3 * H * D, 3 * H * D, D, 1]
+    src = [view(BASE + t * H * D * 2 + p * GB, (B, S_loc, H, D), fused) for t in range(3) for p in range(P)]
+    dst = [view(BASE + (10 + t) * GB, (B, P * S_loc, H // P, D)) for t in range(3)]
+    assert relayout(0, P, 0, src, dst)[0] == LSD_EINVAL
+    assert relayout(3, 0, 0, src, dst)[0] == LSD_EINVAL
+    assert relayout(3, 17, 0, src * 6, dst)[0] == LSD_EUNSUPPORTED
+    r, msg = relayout(3, P, 4, src, dst)
+    assert r == LSD_EINVAL and "rank" in msg
+    # 40 heads cannot be split 3 ways (the pages' divisibility rule)
+    src3 = [view(BASE + p * GB, (B, S_loc, H, D), fused) for p in range(3)]
+    dst3 = [view(BASE + 10 * GB, (B, 3 * S_loc, 13, D))]
+    r, msg = relayout(1, 3, 0, src3, dst3)
+    assert r == LSD_EINVAL and "not divisible" in msg
+    # unequal shard lengths
+    uneq = list(src)
+    uneq[1] = view(BASE + GB, (B, S_loc - 1, H, D), fused)
+    r, msg = relayout(3, P, 0, uneq, dst)
+    assert r == LSD_EINVAL and "same shape" in msg
+    r, msg = relayout(3, P, 0, src, [dst[0], view(BASE + 11 * GB, (B, P * S_loc, H // P + 1, D)), dst[2]])
+    assert r == LSD_EINVAL and "dst[1] shape" in msg
+    r, msg = relayout(3, P, 0, src, [dst[0], dst[0], dst[2]])
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = relayout(3, P, 0, src, [view(BASE + 4096, (B, P * S_loc, H // P, D)), dst[1], dst[2]])
+    assert r == LSD_EINVAL and "overlaps src" in msg
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU memory"):
+        lsd.attn_fwd(q, q, q)

@@ -1,0 +1,110 @@
+"""The four full-size workloads on the GPU, in the launch configuration the
+benchmark times, checked on sampled query rows that the float64 oracle
+computes one by one against the full key set.
+
+Rows per (b, h): a seeded random sample plus the fixed rows {0, 1, 255, 256,
+first row of the ragged last 256-row tile, S_q - 1}."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ref
+from gpu_util import assert_attention_close, err_stats, note, to_bits, to_dev, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+lsd = pytest.importorskip("long_sequence_dit_amd")
+
+N_RANDOM_ROWS = 40
+
+
+def sample_rows(S_q, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    fixed = [0, 1, 255, 256, (S_q // 256) * 256, S_q - 1]
+    rows = np.concatenate([g.choice(S_q, N_RANDOM_ROWS, replace=False), [r for r in fixed if r < S_q]])
+    return np.unique(rows)
+
+
+def check_rows(o_dev, lse_dev, q, k, v, heads, seed, what):
+    """o_dev (B,S_q,H,D) bf16 and lse_dev (B,H,S_q) on the GPU; q/k/v host bits."""
+    B = q.shape[0]
+    S_q = q.shape[1]
+    lse = lse_dev.cpu().numpy()
+    worst = (0.0, 0.0, 0.0)
+    for b in range(B):
+        for h in heads:
+            rows = sample_rows(S_q, seed + 97 * b + h)
+            idx = torch().from_numpy(rows).cuda()
+            og = to_f64(o_dev[b].index_select(0, idx)[:, h])
+            O, L = ref.attention_rows(q, k, v, b, h, rows)
+            mx, mean, rel = assert_attention_close(og, O, lse[b, h, rows], L, f"{what} b={b} h={h}")
+            worst = tuple(max(a, c) for a, c in zip(worst, (mx, mean, rel)))
+    note(f"{what}: worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} rel-rms {worst[2]:.3e}")
+
+
+def test_ltx2_scale():
+    note("full LTX-2: B=1 S=24576 H=32 D=128, RMS-normalised Q/K")
+    t = torch()
+    q, k, v = synth.ltx2_qkv()
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    t.cuda.synchronize()
+    check_rows(o, lse, q, k, v, range(32), 1, "LTX-2")
+
+
+def test_wan_ulysses_share_relayout_then_attention():
+    note("full Wan Ulysses share: fused QKV [2,75600,3,40,128] -> rank slices, P=4")
+    t = torch()
+    B, S, H, D, P = 2, 75_600, 40, 128, 4
+    S_loc = S // P
+    fused = synth.fused_qkv(B, S, H, D, seed=2)
+    f = to_dev(fused)
+    src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    for r in (0, 3):
+        note(f"  relayout rank {r}")
+        qkv = lsd.relayout_seq_to_head(src, P, r)
+        t.cuda.synchronize()
+        hl = H // P
+        for tt in range(3):
+            got = to_bits(qkv[tt])
+            exp = fused[:, :, tt, r * hl:(r + 1) * hl]   # concatenated shards = this rank's head slice
+            assert np.array_equal(got, exp), f"relayout rank {r} tensor {tt}"
+            del got
+        note(f"  attention rank {r}")
+        o, lse = lsd.attn_fwd(*qkv)
+        t.cuda.synchronize()
+        hs = slice(r * hl, (r + 1) * hl)
+        check_rows(o, lse, fused[:, :, 0, hs], fused[:, :, 1, hs], fused[:, :, 2, hs], range(hl), 20 + r,
+                   f"Wan rank {r}")
+        del qkv, o, lse
+
+
+def test_ring_share_blocks_and_merge():
+    note("full Ring/Attention2D share: Q 25200 x 3 K/V blocks of 25200, H=40")
+    t = torch()
+    Sb, H, D = 25_200, 40, 128
+    q, k, v = synth.qkv(1, Sb, 3 * Sb, H, D, seed=3)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    outs, lses = [], []
+    for i in range(3):
+        o, l = lsd.attn_fwd(dq, dk[:, i * Sb:(i + 1) * Sb], dv[:, i * Sb:(i + 1) * Sb])
+        outs.append(o)
+        lses.append(l)
+    om, lm = lsd.attn_merge(outs, lses)
+    ou, lu = lsd.attn_fwd(dq, dk, dv)
+    t.cuda.synchronize()
+    check_rows(om, lm, q, k, v, range(H), 3, "Ring merged")
+    check_rows(ou, lu, q, k, v, range(0, H, 5), 4, "Ring unblocked")
+    # the merge against the oracle's merge of the same bf16 partials, on a row slab
+    rows = slice(25_000, 25_200)
+    Om, Lm = ref.merge([to_bits(o[:, rows]) for o in outs], [l[:, :, rows].cpu().numpy() for l in lses])
+    assert_attention_close(to_f64(om[:, rows]), Om, lm[:, :, rows].cpu().numpy(), Lm, "merge slab")
+
+
+def test_cosmos_long_sequence_with_outlier_keys():
+    note("full Cosmos3-Super share: B=1 S=150000 H=16 D=128, 1% keys x4")
+    t = torch()
+    q, k, v, rows = synth.cosmos_qkv()
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    t.cuda.synchronize()
+    check_rows(o, lse, q, k, v, range(16), 5, "Cosmos")

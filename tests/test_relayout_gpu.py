@@ -1,0 +1,77 @@
+"""relayout_seq_to_head on the GPU (through the C ABI): bit-exact against the
+oracle on random 16-bit patterns (NaN payloads, infinities and -0 included)."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ref
+from gpu_util import note, to_bits, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+lsd = pytest.importorskip("long_sequence_dit_amd")
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("n_tensors", [1, 3])
+def test_all_ranks_bit_exact(P, n_tensors):
+    note(f"relayout P={P} n_tensors={n_tensors}")
+    t = torch()
+    B, S_loc, H, D = 2, 37, 8, 128
+    host = [[synth.random_bits16((B, S_loc, H, D), 1000 * tt + 10 * P + p) for p in range(P)]
+            for tt in range(n_tensors)]
+    dev = [[to_dev(x) for x in row] for row in host]
+    for r in range(P):
+        outs = lsd.relayout_seq_to_head(dev, P, r)
+        t.cuda.synchronize()
+        for tt in range(n_tensors):
+            assert np.array_equal(to_bits(outs[tt]), ref.relayout_seq_to_head(host[tt], P, r))
+
+
+def test_fused_qkv_strided_source():
+    note("relayout fused QKV [2,4*25,3,40,128] -> 3 x [2,100,10,128], P=4")
+    t = torch()
+    B, S_loc, H, D, P = 2, 25, 40, 128, 4
+    host = synth.random_bits16((B, P * S_loc, 3, H, D), 5)
+    f = to_dev(host)
+    # shard p of tensor t is a strided view into the fused buffer
+    src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    assert src[2][1].stride() == (P * S_loc * 3 * H * D, 3 * H * D, D, 1)
+    for r in range(P):
+        outs = lsd.relayout_seq_to_head(src, P, r)
+        t.cuda.synchronize()
+        for tt in range(3):
+            chunks = [host[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)]
+            assert np.array_equal(to_bits(outs[tt]), ref.relayout_seq_to_head(chunks, P, r))
+
+
+def test_non_contiguous_heads_and_guard_bands():
+    note("relayout head-strided destination + guard bands")
+    t = torch()
+    B, S_loc, H, D, P = 1, 19, 6, 64, 2
+    host = [synth.random_bits16((B, S_loc, H, D), 300 + p) for p in range(P)]
+    dev = [to_dev(x) for x in host]
+    sentinel = -12345
+    big = t.full((B, P * S_loc, 2 * (H // P) + 2, D), sentinel, dtype=t.int16, device="cuda")
+    dst = big.view(t.bfloat16)[:, :, 1:1 + 2 * (H // P):2]     # every other head slot
+    lsd.relayout_seq_to_head([dev], P, 1, dst=[dst])
+    t.cuda.synchronize()
+    assert np.array_equal(to_bits(dst), ref.relayout_seq_to_head(host, P, 1))
+    bb = big.cpu().numpy()
+    assert (bb[:, :, 0] == sentinel).all() and (bb[:, :, 2:2 * (H // P) + 1:2] == sentinel).all()
+    assert (bb[:, :, -1] == sentinel).all()
+
+
+def test_round_trip_byte_exact():
+    note("relayout round trip (gather(send(x)) == x)")
+    t = torch()
+    B, S_loc, H, D, P = 2, 33, 12, 128, 4
+    host = [synth.random_bits16((B, S_loc, H, D), 400 + p) for p in range(P)]
+    dev = [to_dev(x) for x in host]
+    ys = []
+    for r in range(P):
+        ys.append(to_bits(lsd.relayout_seq_to_head([dev], P, r)[0]))
+    t.cuda.synchronize()
+    for p in range(P):
+        assert np.array_equal(ref.relayout_head_to_seq(ys, P, p), host[p])
