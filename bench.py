@@ -214,7 +214,7 @@ def cpu_baseline(pipe, budget_s):
     g = np.random.Generator(np.random.PCG64(123))
     heads = [(b, hh) for b in range(B) for hh in range(Hq)]
     i = 0
-    while t_attn < budget_s and i < 4 * len(heads):
+    while t_attn < budget_s and i < 64 * len(heads):
         b, hh = heads[i % len(heads)]
         r0 = int(g.integers(0, max(1, pipe.S_q - 256)))
         rows = np.arange(r0, min(pipe.S_q, r0 + 256))

@@ -16,10 +16,13 @@
 //   row sum are in-lane, with one permlane32 swap to combine the two lane halves.
 // * The same accumulator registers, rounded to bf16, are directly the B operand
 //   (P^T) of the PV product O^T = V^T P^T; the key order inside the 16-wide
-//   reduction is permuted to match the accumulator layout, and the A operand
-//   (V^T) is read from the row-major V tile with ds_read_b64_tr_b16.
-// * K/V tiles of 64 keys are staged through LDS, double-buffered: the global
-//   loads of tile t+1 are in flight while tile t is computed.
+//   reduction is permuted to match the accumulator layout.
+// * V is transposed in registers on its way into LDS (key pairs packed with
+//   v_perm), so each PV A operand is one 16-byte LDS read; K is stored
+//   row-major.  K/V tiles of 64 keys are double-buffered in LDS and their
+//   global loads are issued one iteration ahead.
+// * Ping-pong: the two waves that share a SIMD run half an iteration apart, so
+//   one streams MFMAs while the other does the softmax arithmetic.
 // * The row max is tracked lazily: O and l are rescaled only when a row's max
 //   grows by more than 2^8 (in the exp2 domain), which keeps exp2 arguments
 //   <= 8; the final O / l and LSE are exact for any reference max.
@@ -39,28 +42,28 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;  // query rows per workgroup
-constexpr int kBlockN = 64;           // keys per LDS tile
+constexpr int kBlockM = kWaves * 32;       // query rows per workgroup
+constexpr int kBlockN = 64;                // keys per LDS tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D>
 struct Cfg {
-  // LDS row pitches (elements).  K rows are skewed by 16 B so that 16 lanes
-  // reading one 16-B column of 16 rows hit distinct banks; V rows by 64 B so
-  // that the 4-row x 64-B footprint of a transposed read by 32 lanes does.
+  // K row pitch (elements): 16-byte skew per row, so 16 lanes reading one
+  // 16-byte column of 16 consecutive rows hit distinct banks.
   static constexpr int kRowK = D + 8;
-  static constexpr int kRowV = D + 32;
-  static constexpr int kDSteps = D / 16;                  // QK^T reduction steps
-  static constexpr int kDBlocks = D / 32;                 // O^T row blocks
-  static constexpr int kChunksPerRow = D / 8;             // 16-B chunks per row
-  static constexpr int kLoadsPerThread = kBlockN * kChunksPerRow / kThreads;  // per tensor
-  static constexpr int kLdsK = kBlockN * kRowK;           // elements per buffer
-  static constexpr int kLdsV = kBlockN * kRowV;
+  // V is stored transposed, V^T[d][vt_pos(j)], 64 keys per row in the order the
+  // PV MFMA consumes them; a pitch of 72 elements (36 dwords) makes both the
+  // transposing 4-byte writes and the 16-byte operand reads conflict-free.
+  static constexpr int kRowVT = 72;
+  static constexpr int kDSteps = D / 16;           // QK^T reduction steps
+  static constexpr int kDBlocks = D / 32;          // O^T row blocks
+  static constexpr int kChunksPerRow = D / 8;      // 16-byte chunks per row
+  static constexpr int kLoadsPerThread = kBlockN * kChunksPerRow / kThreads;  // K chunks per thread
+  static constexpr int kLdsK = kBlockN * kRowK;    // elements per K buffer
+  static constexpr int kLdsV = D * kRowVT;         // elements per V^T buffer
 };
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
@@ -79,13 +82,21 @@ __device__ inline float partner_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Position of key j (0..63) inside a V^T row.  The PV MFMA's 16-wide
+// reduction slot e of lane half hh carries key 8*(e/4) + 4*hh + e%4 of its
+// 16-key group (the order in which the S^T accumulator holds the weights), so
+// each lane half's 8 keys are stored contiguously.
+__device__ __host__ constexpr int vt_pos(int j) {
+  return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j & 15) >> 3) + (j & 3);
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::kLdsK + C::kLdsV)];
-  uint16_t* Ks = smem;                    // [2][kBlockN][kRowK]
-  uint16_t* Vs = smem + 2 * C::kLdsK;     // [2][kBlockN][kRowV]
+  uint16_t* Ks = smem;                 // [2][kBlockN][kRowK]
+  uint16_t* Vs = smem + 2 * C::kLdsK;  // [2][D][kRowVT], V transposed
 
   // ---- XCD-aware tile order: dispatch is round-robin over 8 XCDs; give each
   // XCD a contiguous range of (b, h, q-tile) so its CUs share K/V in L2.
@@ -107,110 +118,108 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
 
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  const int n_tiles = (a.S_kv + kBlockN - 1) / kBlockN;  // >= 1 (S_kv == 0 never gets here)
 
   // ---- Q rows of this wave, as MFMA B operands (k = head channel).
   const int qrow = qt * kBlockM + wave * 32 + l32;
   const bool qvalid = qrow < a.S_q;
   bf16x8 qreg[C::kDSteps];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qrow * a.q_ss + (int64_t)h * a.q_sh + 8 * hh;
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)min(qrow, a.S_q - 1) * a.q_ss + (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::kDSteps; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qvalid) v = *(const u32x4*)(qp + 16 * s);
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
+      if (!qvalid) v = (u32x4){0u, 0u, 0u, 0u};
       qreg[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  // ---- global -> register staging of one K/V tile (rows beyond S_kv are zero)
-  const int n_tiles = (a.S_kv + kBlockN - 1) / kBlockN;
-  u32x4 kst[C::kLoadsPerThread], vst[C::kLoadsPerThread];
-  auto load_tile = [&](int t) {
+  // ---- global -> register -> LDS staging.  Rows past S_kv are read from the
+  // last valid row instead (finite data, no branch): their scores are masked
+  // to -inf, so they get zero weight.
+  const int last_row = a.S_kv - 1;
+  int k_row[C::kLoadsPerThread], k_ch[C::kLoadsPerThread];
+#pragma unroll
+  for (int u = 0; u < C::kLoadsPerThread; ++u) {
+    const int idx = tid + kThreads * u;
+    k_row[u] = idx / C::kChunksPerRow;
+    k_ch[u] = idx % C::kChunksPerRow;
+  }
+  // V: thread -> (key pair, 16-byte d-chunk); each wave covers all 32 pairs of
+  // a tile for two chunks, which keeps the transposing writes conflict-free.
+  // For D = 64 only waves 0-3 carry V.
+  const int vp_pair = (tid & 63) >> 1;
+  const bool v_loader = 2 * (tid >> 6) + (tid & 1) < C::kChunksPerRow;
+  const int vp_chunk = v_loader ? 2 * (tid >> 6) + (tid & 1) : 0;
+  u32x4 kst[C::kLoadsPerThread], vst[2];
+  auto load_k = [&](int t) {
+    const int r0 = t * kBlockN;
 #pragma unroll
     for (int u = 0; u < C::kLoadsPerThread; ++u) {
-      const int idx = tid + kThreads * u;
-      const int row = idx / C::kChunksPerRow;
-      const int ch = idx % C::kChunksPerRow;
-      const int j = t * kBlockN + row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (j < a.S_kv) {
-        kv = *(const u32x4*)(kbase + (int64_t)j * a.k_ss + 8 * ch);
-        vv = *(const u32x4*)(vbase + (int64_t)j * a.v_ss + 8 * ch);
-      }
-      kst[u] = kv;
-      vst[u] = vv;
+      const int j = min(r0 + k_row[u], last_row);
+      kst[u] = *(const u32x4*)(kbase + (int64_t)j * a.k_ss + 8 * k_ch[u]);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto load_v = [&](int t) {
+    const int r0 = t * kBlockN + 2 * vp_pair;
 #pragma unroll
-    for (int u = 0; u < C::kLoadsPerThread; ++u) {
-      const int idx = tid + kThreads * u;
-      const int row = idx / C::kChunksPerRow;
-      const int ch = idx % C::kChunksPerRow;
-      *(u32x4*)(Ks + buf * C::kLdsK + row * C::kRowK + 8 * ch) = kst[u];
-      *(u32x4*)(Vs + buf * C::kLdsV + row * C::kRowV + 8 * ch) = vst[u];
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(r0 + u, last_row);
+      vst[u] = *(const u32x4*)(vbase + (int64_t)j * a.v_ss + 8 * vp_chunk);
     }
+  };
+  auto store_k = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < C::kLoadsPerThread; ++u)
+      *(u32x4*)(Ks + (t & 1) * C::kLdsK + k_row[u] * C::kRowK + 8 * k_ch[u]) = kst[u];
+  };
+  // V^T[d][vt_pos(j)]: for each of the 8 channels d of the chunk, one dword
+  // holding (V[2p][d], V[2p+1][d]); vt_pos keeps key pairs adjacent.
+  const int vt_col = vt_pos(2 * vp_pair);
+  auto store_v = [&](int t) {
+    uint16_t* dst = Vs + (t & 1) * C::kLdsV + (8 * vp_chunk) * C::kRowVT + vt_col;
+    if (C::kChunksPerRow == 16 || v_loader) {  // every thread carries V when D = 128
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = __builtin_amdgcn_perm(vst[1][e >> 1], vst[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        *(uint32_t*)(dst + e * C::kRowVT) = w;
+      }
+    }
+  };
+  // Workgroup barrier that orders LDS only: outstanding global prefetches stay
+  // in flight across it.
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
   f32x16 oacc[C::kDBlocks];
 #pragma unroll
-  for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  for (int db = 0; db < C::kDBlocks; ++db) oacc[db] = (f32x16){};
   float m_run = -INFINITY;  // running reference max, log2 domain
   float l_run = 0.0f;       // this lane's partial row sum
   const float c = a.scale_log2;
+  f32x16 sacc[2];           // S^T of the tile being processed
+  uint32_t pk[2][8];        // its weights, bf16 pairs
 
-  // per-lane constant parts of the transposed V read address
-  const int tr_i = lane & 15;
-  const int tr_row = 4 * hh + (tr_i >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-
-    const uint16_t* Kt = Ks + buf * C::kLdsK;
-    const uint16_t* Vt = Vs + buf * C::kLdsV;
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-      const uint16_t* kp = Kt + (32 * kb + l32) * C::kRowK + 8 * hh;
-#pragma unroll
-      for (int s = 0; s < C::kDSteps; ++s) {
-        bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * s));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys beyond S_kv (last tile only)
+  // ---- VALU phase SM(t): mask, row max, lazy rescale, exp
+  auto mask_tail = [&](int t) {
     const int kv0 = t * kBlockN;
-    if (kv0 + kBlockN > a.S_kv) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= a.S_kv) sacc[kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (exp2 domain, lazy rescale)
-    float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int j = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (j >= a.S_kv) sacc[kb][r] = -INFINITY;
+      }
+  };
+  auto softmax = [&]() {
+    float mx = __builtin_fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[0][r], sacc[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[1][r], sacc[1][r + 1]));
     mx = partner_max(mx) * c;
     const float m_new = fmaxf(m_run, mx);
     const bool need = m_new > m_run + kRescaleThreshold;
@@ -223,11 +232,11 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    // P = exp2(S c - m) rounded to bf16.  The tile's 32 weights are summed on
+    // their own before joining the running sum: added one by one to a sum
+    // dominated by a few large weights (outlier keys), the many small ones
+    // would fall below half an ulp and be lost.
     const float neg_m = -m_run;
-    uint32_t pk[2][8];
-    // The tile's 32 weights are summed on their own before joining the running
-    // sum: added one by one to a sum dominated by a few large weights (outlier
-    // keys), the many small ones would fall below half an ulp and be lost.
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -240,46 +249,134 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
         pk[kb][r >> 1] = pack_bf16(p0, p1);
       }
     l_run += lt0 + lt1;
+  };
 
-    // ---- O^T += V^T P^T
+  // ---- MFMA phase G(t) = PV(t) then QK(t+1), as a fixed list of steps.  Step
+  // i issues the LDS read of the operand that step i + kDist consumes, then its
+  // own MFMA; sched_barrier fences keep this order, so kDist reads are always
+  // in flight and one wave streams MFMAs back to back.  The staging of
+  // K_{t+2} / V_{t+1} into LDS and the global loads of K_{t+3} / V_{t+2} ride
+  // on fixed steps.
+  constexpr int kPvSteps = 4 * C::kDBlocks;  // (kb, ks, db)
+  constexpr int kQkSteps = 2 * C::kDSteps;   // (kb, s2)
+  constexpr int kSteps = kPvSteps + kQkSteps;
+  constexpr int kDist = 4;
+  auto frag_ptr = [&](int i, int t) -> const uint16_t* {
+    if (i < kPvSteps) {
+      const int kb = i / (2 * C::kDBlocks), ks = (i / C::kDBlocks) & 1, db = i % C::kDBlocks;
+      return Vs + (t & 1) * C::kLdsV + (32 * db + l32) * C::kRowVT + 8 * hh + 16 * (2 * kb + ks);
+    }
+    const int j = i - kPvSteps;
+    const int kb = j / C::kDSteps, s2 = j % C::kDSteps;
+    return Ks + ((t + 1) & 1) * C::kLdsK + (32 * kb + l32) * C::kRowK + 8 * hh + 16 * s2;
+  };
+  auto mfma_phase = [&](int t) {
+    u32x4 fr[kDist];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < kDist; ++i) fr[i] = *(const u32x4*)frag_ptr(i, t);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pv = {pk[kb][4 * ks + 0], pk[kb][4 * ks + 1], pk[kb][4 * ks + 2], pk[kb][4 * ks + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-        const uint16_t* vp = Vt + (32 * kb + 16 * ks + tr_row) * C::kRowV + tr_col;
-#pragma unroll
-        for (int db = 0; db < C::kDBlocks; ++db) {
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db));
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::kRowV + 32 * db));
-          u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[db], 0, 0, 0);
-        }
+    for (int i = 0; i < kSteps; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 cur = fr[i % kDist];
+      if (i + kDist < kSteps) fr[i % kDist] = *(const u32x4*)frag_ptr(i + kDist, t);
+      if (i < kPvSteps) {
+        const int kb = i / (2 * C::kDBlocks), ks = (i / C::kDBlocks) & 1, db = i % C::kDBlocks;
+        const u32x4 pv4 = {pk[kb][4 * ks + 0], pk[kb][4 * ks + 1], pk[kb][4 * ks + 2], pk[kb][4 * ks + 3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur),
+                                                            __builtin_bit_cast(bf16x8, pv4), oacc[db], 0, 0, 0);
+      } else {
+        const int j = i - kPvSteps;
+        const int kb = j / C::kDSteps, s2 = j % C::kDSteps;
+        const f32x16 acc_in = (s2 == 0) ? (f32x16){} : sacc[kb];
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur), qreg[s2], acc_in, 0, 0, 0);
       }
+      if (i == 2) store_k(t + 2);
+      if (i == 3) store_v(t + 1);
+      if (i == 6) load_k(t + 3);
+      if (i == 8) load_v(t + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    if (t + 1 < n_tiles) {
-      store_tile(buf ^ 1);
-      __syncthreads();
+  // ---- Ping-pong schedule.  Waves w and w+4 share a SIMD; group A (waves
+  // 0-3) runs one barrier interval ahead of group B (waves 4-7), so in every
+  // interval one wave of each SIMD is in its MFMA phase G(t) while the other is
+  // in its VALU phase SM(t):
+  //   A: QK(0) SM(0) | G(0) | SM(1) | G(1) | ...
+  //   B: QK(0)       | SM(0) | G(0) | SM(1) | ...
+  // LDS: K_t lives in K buffer t%2 and is read during intervals 2t-1 (A) and 2t
+  // (B); V_t in V buffer t%2 during 2t+1 (A) and 2t+2 (B).  Both groups write
+  // their chunks of K_{t+2} and V_{t+1} during their G(t) (intervals 2t+1 and
+  // 2t+2), after every reader of those buffers has passed a barrier, and issue
+  // the global loads of K_{t+3} and V_{t+2}, in flight for one iteration.  Past
+  // the last tile these reads and writes touch stale buffers (clamped global
+  // addresses) whose results are never used.
+  const int group = wave >> 2;
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
+  __syncthreads();
+  load_k(2);
+  load_v(1);
+
+  {  // QK(0)
+    const uint16_t* kp = Ks + l32 * C::kRowK + 8 * hh;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = (f32x16){};
+#pragma unroll
+      for (int s2 = 0; s2 < C::kDSteps; ++s2)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 32 * kb * C::kRowK + 16 * s2)), qreg[s2], sacc[kb], 0, 0, 0);
     }
   }
+  if (group == 1) lds_barrier();
+  for (int t = 0; t < n_tiles; ++t) {
+    if ((t + 1) * kBlockN > a.S_kv) mask_tail(t);
+    softmax();
+    lds_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase(t);
+    __builtin_amdgcn_s_setprio(0);
+    lds_barrier();
+  }
+  if (group == 0) lds_barrier();
 
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l)
   const float l_tot = partner_sum(l_run);
-  if (!qvalid) return;
   const float inv = 1.0f / l_tot;
-  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)qrow * a.o_ss + (int64_t)h * a.o_sh + 4 * hh;
+  // Stage this wave's 32 x D output tile through LDS (the K/V buffers are free
+  // once every wave has left the loop) so that global stores write whole
+  // 256-byte rows instead of 8-byte pieces of 32 different rows.
+  __syncthreads();
+  constexpr int kRowO = D + 4;  // pitch (elements): rows land on distinct bank pairs
+  uint16_t* Ow = smem + wave * 32 * kRowO;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
                  pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-      *(u32x2*)(op + 32 * db + 8 * g) = w;
+      *(u32x2*)(Ow + l32 * kRowO + 32 * db + 8 * g + 4 * hh) = w;
     }
-  if (a.lse != nullptr && hh == 0)
+  if (a.lse != nullptr && hh == 0 && qvalid)
     a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  // rows are written by 64 lanes: lane = (row r in 0..64/CPR-1, 16-B chunk)
+  constexpr int kCPR = D / 8;  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kCPR;
+  const int ch = lane % kCPR;
+  const int r0 = lane / kCPR;
+  const int row_base = qt * kBlockM + wave * 32;
+  uint16_t* obase = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 8 * ch;
+#pragma unroll
+  for (int r = r0; r < 32; r += kRowsPerPass) {
+    const u32x4 v = *(const u32x4*)(Ow + r * kRowO + 8 * ch);
+    const int row = row_base + r;
+    if (row < a.S_q) *(u32x4*)(obase + (int64_t)row * a.o_ss) = v;
+  }
 }
 
 // S_kv == 0: no keys, O = 0 and LSE = -inf (one thread per 8 output elements).
