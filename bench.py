@@ -18,8 +18,9 @@ the dominant kernel (attention) with HIP events on the stream it runs on;
 peak); ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of
 the same work on this host and extrapolates it to one step.
 
-Other workloads (--workload): wan (Ulysses share: relayout P=4 -> attention),
-ring (three K/V blocks + merge), cosmos (S=150,000), tiny.
+Other workloads (--workload): wan (Ulysses share: relayout P=4 -> attention ->
+inverse relayout of the output back to this rank's sequence shard), ring
+(three K/V blocks + merge), cosmos (S=150,000), tiny.
 """
 
 from __future__ import annotations
@@ -44,8 +45,9 @@ WORKLOADS = {
     "ltx2": dict(desc="LTX-2 scale: fused QKV [1,24576,3,32,128] -> relayout (P=1) -> attention over 2 K/V "
                       "blocks with fp32 LSE -> LSE merge", B=1, S=24_576, H=32, D=128, P=1, kv_blocks=2, seed=1),
     "wan": dict(desc="Wan 2.2 A14B Ulysses share: fused QKV [2,75600,3,40,128] -> relayout P=4 rank 0 "
-                     "-> attention [2,75600,10,128] with fp32 LSE", B=2, S=75_600, H=40, D=128, P=4, kv_blocks=1,
-                seed=2),
+                     "-> attention [2,75600,10,128] with fp32 LSE -> inverse relayout of O (this rank's slice "
+                     "and 3 stand-in slices of the other ranks) -> shard [2,18900,40,128]", B=2, S=75_600, H=40,
+                D=128, P=4, kv_blocks=1, seed=2),
     "ring": dict(desc="Ring/Attention2D share: Q [1,25200,40,128] vs 3 K/V blocks of 25200 with fp32 LSE "
                       "-> LSE merge (n=3)", B=1, S=25_200, H=40, D=128, P=None, kv_blocks=3, seed=3),
     "cosmos": dict(desc="Cosmos3-Super share: Q,K,V [1,150000,16,128], 1% of keys x4, with fp32 LSE", B=1,
@@ -123,6 +125,21 @@ class Pipeline:
             self.lse = torch.empty((B, Hq, self.S_q), dtype=torch.float32, device="cuda")
         self.has_relayout = name in ("ltx2", "tiny", "wan")
         self.has_merge = nb > 1
+        # Ulysses output side: with P > 1 the attention output goes back to
+        # sequence shard 0; the other ranks' head slices are seeded stand-ins.
+        self.has_inverse = self.has_relayout and w["P"] > 1
+        if self.has_inverse:
+            P = w["P"]
+            g = torch.Generator(device="cuda")
+            g.manual_seed(w["seed"] * 1000 + 7)
+            self.o_final = self.o if nb > 1 else self.o_parts[0]
+            others = [torch.randn(self.o_final.shape, generator=g, device="cuda", dtype=torch.float32)
+                      .to(torch.bfloat16) for _ in range(P - 1)]
+            self.inv_src = [[self.o_final] + others]
+            self.shard = torch.empty((B, self.S_q // P, P * Hq, D), dtype=torch.bfloat16, device="cuda")
+            self.inverse_bytes = 2 * 2 * B * (self.S_q // P) * P * Hq * D
+        else:
+            self.inverse_bytes = 0
         B_, D_ = B, D
         self.flops = 4.0 * B_ * Hq * self.S_q * self.S_kv * D_
         n_rel = 3 * B_ * self.S_q * Hq * D_
@@ -155,10 +172,23 @@ class Pipeline:
             mark()
             lsd.attn_merge(self.o_parts, self.lse_parts, o=self.o, lse=self.lse)
             mark()
+        if self.has_inverse:
+            mark()
+            lsd.relayout_head_to_seq(self.inv_src, self.w["P"], 0, dst=[self.shard])
+            mark()
         return k
 
+    def kernel_names(self):
+        names = ["relayout"] if self.has_relayout else []
+        names += ["attn_fwd"] * len(self.bounds)
+        if self.has_merge:
+            names.append("attn_merge")
+        if self.has_inverse:
+            names.append("relayout_inv")
+        return names
+
     def n_events(self):
-        return 2 * (int(self.has_relayout) + len(self.bounds) + int(self.has_merge))
+        return 2 * len(self.kernel_names())
 
 
 def kernel_source_hash():
@@ -235,7 +265,16 @@ def cpu_baseline(pipe, budget_s):
         t0 = time.perf_counter()
         ref.merge(parts, lses)
         t_merge_full = (time.perf_counter() - t0) * pipe.S_q / S_slab
-    t_step = t_rel + t_attn_full + t_merge_full
+    # inverse relayout: the oracle's copy over P stand-in head slices, timed in full
+    t_inv = 0.0
+    if pipe.has_inverse:
+        P = w["P"]
+        slices = [np.full((B, pipe.S_q, Hq, D), r, dtype=np.uint16) for r in range(P)]
+        t0 = time.perf_counter()
+        ref.relayout_head_to_seq(slices, P, 0)
+        t_inv = time.perf_counter() - t0
+        del slices
+    t_step = t_rel + t_attn_full + t_merge_full + t_inv
     return {
         "value": pipe.flops / t_step / 1e12,
         "unit": "TFLOP/s",
@@ -245,6 +284,7 @@ def cpu_baseline(pipe, budget_s):
                    f"({t_attn:.1f} s), extrapolated to {total_rows} rows"
                    + (f"; relayout timed in full ({t_rel:.2f} s)" if t_rel else "")
                    + (f"; merge timed on a {min(pipe.S_q, 512)}-position slab, scaled" if pipe.has_merge else "")
+                   + (f"; inverse relayout timed in full ({t_inv:.2f} s)" if pipe.has_inverse else "")
                    + f"; extrapolated step {t_step:.1f} s; host has {cores} cores, BLAS threads {blas_threads}"),
     }
 
@@ -290,12 +330,7 @@ def main():
     ms_step = 1e3 * wall / args.steps
 
     # per-kernel durations from the events (same stream as the kernels)
-    names = []
-    if pipe.has_relayout:
-        names.append("relayout")
-    names += ["attn_fwd"] * len(pipe.bounds)
-    if pipe.has_merge:
-        names.append("attn_merge")
+    names = pipe.kernel_names()
     dur = {n: [] for n in set(names)}
     attn_flops = []
     for s in range(args.steps):
@@ -320,6 +355,11 @@ def main():
         gbs = pipe.merge_bytes / (ms * 1e-3) / 1e9
         kernels["attn_merge"] = {"avg_ms": round(ms, 4), "bytes": pipe.merge_bytes, "GB/s": round(gbs, 1),
                                  "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    if pipe.has_inverse:
+        ms = float(np.mean(dur["relayout_inv"]))
+        gbs = pipe.inverse_bytes / (ms * 1e-3) / 1e9
+        kernels["relayout_inv"] = {"avg_ms": round(ms, 4), "bytes": pipe.inverse_bytes, "GB/s": round(gbs, 1),
+                                   "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
     traffic = load_traffic(args.workload)
     flops_per_launch = float(np.mean(pipe.attn_flops_per_launch))

@@ -1,12 +1,14 @@
 /*
  * lsd.h - C ABI of the long-sequence DiT attention library (MI355X, gfx950).
  *
- * Three calls make up the hot path of one sequence-parallel DiT attention
+ * Four calls make up the hot path of one sequence-parallel DiT attention
  * layer on one GPU:
  *
  *   lsd_relayout_seq_to_head  seq-major shards -> head-major slice (Ulysses)
  *   lsd_attn_fwd              dense bidirectional attention, O and optional LSE
  *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
+ *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
+ *                             after attention)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -83,8 +85,9 @@ const char* lsd_last_error(void);
  * S_q and S_kv may differ (a query block against a key/value block).
  * S_kv == 0 gives O = 0 and LSE = -inf.  Zero-sized B, S_q or H is a no-op.
  * softmax_scale <= 0 (or NaN) selects 1/sqrt(D); +inf is rejected.
- * D must be 64 or 128 (LSD_EUNSUPPORTED otherwise).  The device must be
- * gfx950 (LSD_EUNSUPPORTED otherwise).
+ * D must be 64 or 128, and the sequence strides of k and v must be below
+ * 2^24 elements (LSD_EUNSUPPORTED otherwise).  The device must be gfx950
+ * (LSD_EUNSUPPORTED otherwise).
  */
 lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
                         const lsd_view4* o, float* lse, float softmax_scale, void* stream);
@@ -133,6 +136,32 @@ lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* l
  * otherwise).  Destinations may not overlap any source or each other.
  */
 lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src,
+                                    const lsd_view4* dst, void* stream);
+
+/*
+ * Ulysses head-major -> sequence-major relayout for one destination rank: the
+ * inverse of lsd_relayout_seq_to_head, run on the attention output.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+ * "Ulysses Parallelism" and its Figure 2 (after the full-sequence attention
+ * the [B, S, H/P, D] head slices are converted back to the [B, S/P, H, D]
+ * sequence shards the MLP works on), and by "How 8 GPUs split tokens: what
+ * LTX-2's sequence-parallel all2all moves", "Precise statement" (the round
+ * trip through both exchanges returns every byte).
+ *
+ *   src  n_tensors * P views, index t*P + r: rank r's head slice of tensor t,
+ *        each (B, P*S_loc, H_loc, D); all of one shape.
+ *   dst  n_tensors views, each (B, S_loc, P*H_loc, D), written.
+ *
+ *   dst[t][b, s, r*H_loc + j, :] = src[t*P + r][b, rank*S_loc + s, j, :]
+ *
+ * So lsd_relayout_head_to_seq(rank p) applied to the P outputs of
+ * lsd_relayout_seq_to_head(rank 0..P-1) returns sequence shard p bit for bit.
+ * A pure 16-bit copy.  1 <= n_tensors <= 3, 1 <= P <= 16, 0 <= rank < P, and
+ * P must divide the slices' sequence length (LSD_EINVAL otherwise).
+ * Destinations may not overlap any source or each other.
+ */
+lsd_status lsd_relayout_head_to_seq(int n_tensors, int P, int rank, const lsd_view4* src,
                                     const lsd_view4* dst, void* stream);
 
 #ifdef __cplusplus

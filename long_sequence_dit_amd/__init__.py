@@ -53,6 +53,9 @@ def lib():
         L.lsd_relayout_seq_to_head.restype = ctypes.c_int
         L.lsd_relayout_seq_to_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
+        L.lsd_relayout_head_to_seq.restype = ctypes.c_int
+        L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
+                                               P(View4), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -170,4 +173,29 @@ def relayout_seq_to_head(src: Sequence[Sequence], P: int, rank: int, dst: Option
     dv = (View4 * nt)(*[_view(d, f"dst[{t}]") for t, d in enumerate(dst)])
     st = lib().lsd_relayout_seq_to_head(nt, P, rank, sv, dv, _stream(src[0][0]))
     _check(st, "lsd_relayout_seq_to_head")
+    return dst
+
+
+def relayout_head_to_seq(src: Sequence[Sequence], P: int, rank: int, dst: Optional[List] = None):
+    """Ulysses head-major -> seq-major relayout for destination ``rank`` (the
+    inverse of ``relayout_seq_to_head``, run on the attention output).
+
+    src: one list per tensor (1 to 3 of them), each holding the P ranks' head
+    slices (B, P*S_loc, H_loc, D).  Returns one (B, S_loc, P*H_loc, D) tensor per
+    source tensor: sequence shard ``rank`` with every head.
+    """
+    torch = _torch()
+    nt = len(src)
+    if nt == 0 or any(len(s) != P for s in src):
+        raise ValueError("relayout_head_to_seq: src must be n_tensors lists of P head slices each")
+    B, S, H_loc, D = src[0][0].shape
+    if dst is None:
+        if S % P != 0:
+            raise ValueError(f"relayout_head_to_seq: sequence length S={S} is not divisible by P={P}")
+        dst = [torch.empty((B, S // P, P * H_loc, D), dtype=src[0][0].dtype, device=src[0][0].device)
+               for _ in range(nt)]
+    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{r}]") for t, s in enumerate(src) for r, c in enumerate(s)])
+    dv = (View4 * nt)(*[_view(d, f"dst[{t}]") for t, d in enumerate(dst)])
+    st = lib().lsd_relayout_head_to_seq(nt, P, rank, sv, dv, _stream(src[0][0]))
+    _check(st, "lsd_relayout_head_to_seq")
     return dst

@@ -145,6 +145,10 @@ lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4*
   if (!same_shape(*v, *k)) return fail(LSD_EINVAL, "v shape must equal k shape (B, S_kv, H, D)");
   if (!same_shape(*o, *q)) return fail(LSD_EINVAL, "o shape must equal q shape (B, S_q, H, D)");
   if (D != 64 && D != 128) return fail(LSD_EUNSUPPORTED, "head dim D=%lld unsupported (64 or 128)", (long long)D);
+  // a 64-key K/V tile is addressed with 32-bit byte offsets
+  if (k->stride[1] >= (int64_t(1) << 24) || v->stride[1] >= (int64_t(1) << 24))
+    return fail(LSD_EUNSUPPORTED, "k/v sequence stride (%lld, %lld elements) must be below 2^24",
+                (long long)k->stride[1], (long long)v->stride[1]);
   if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
   if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
   if (B * S_q * H == 0) return ok();
@@ -221,8 +225,15 @@ lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* l
   return launched(lsd::launch_attn_merge(a, (hipStream_t)stream), "attn_merge");
 }
 
-lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,
-                                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of both Ulysses relayouts.
+//   forward: src (B, S_loc, H, D) x P shards -> dst (B, P*S_loc, H/P, D)
+//   inverse: src (B, P*S_loc, H_loc, D) x P rank slices -> dst (B, S_loc, P*H_loc, D)
+lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank, const lsd_view4* src,
+                    const lsd_view4* dst, void* stream) {
   if (n_tensors < 1 || n_tensors > lsd::kMaxRelayoutTensors)
     return fail(LSD_EINVAL, "n_tensors=%d: must be 1..%d (Q, K, V)", n_tensors, lsd::kMaxRelayoutTensors);
   if (P < 1) return fail(LSD_EINVAL, "P=%d: sequence-parallel degree must be >= 1", P);
@@ -232,22 +243,36 @@ lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_vi
   lsd_status s;
   char name[48];
   for (int i = 0; i < n_tensors * P; ++i) {
-    std::snprintf(name, sizeof name, "src[%d] (tensor %d, shard %d)", i, i / P, i % P);
+    std::snprintf(name, sizeof name, "src[%d] (tensor %d, %s %d)", i, i / P, inverse ? "rank" : "shard", i % P);
     if ((s = check_view(name, &src[i])) != LSD_OK) return s;
     if (!same_shape(src[i], src[0]))
-      return fail(LSD_EINVAL, "src[%d]: sequence shards must all have the same shape (B, S_loc, H, D)", i);
+      return fail(LSD_EINVAL, inverse ? "src[%d]: head slices must all have the same shape (B, S, H_loc, D)"
+                                       : "src[%d]: sequence shards must all have the same shape (B, S_loc, H, D)",
+                  i);
   }
-  const int64_t B = src[0].shape[0], S_loc = src[0].shape[1], H = src[0].shape[2], D = src[0].shape[3];
-  if (H % P != 0) return fail(LSD_EINVAL, "head count H=%lld is not divisible by P=%d", (long long)H, P);
-  const int64_t H_loc = H / P;
+  const int64_t B = src[0].shape[0], D = src[0].shape[3];
+  int64_t S_loc, H_loc;
+  if (!inverse) {
+    S_loc = src[0].shape[1];
+    const int64_t H = src[0].shape[2];
+    if (H % P != 0) return fail(LSD_EINVAL, "head count H=%lld is not divisible by P=%d", (long long)H, P);
+    H_loc = H / P;
+  } else {
+    const int64_t S = src[0].shape[1];
+    if (S % P != 0)
+      return fail(LSD_EINVAL, "sequence length S=%lld is not divisible by P=%d (equal shards)", (long long)S, P);
+    S_loc = S / P;
+    H_loc = src[0].shape[2];
+  }
   if ((int64_t)P * S_loc > 0x7fffffff) return fail(LSD_EINVAL, "P*S_loc exceeds 2^31-1");
+  const int64_t want1 = inverse ? S_loc : P * S_loc, want2 = inverse ? P * H_loc : H_loc;
   for (int t = 0; t < n_tensors; ++t) {
     std::snprintf(name, sizeof name, "dst[%d]", t);
     if ((s = check_view(name, &dst[t])) != LSD_OK) return s;
     const lsd_view4& d = dst[t];
-    if (d.shape[0] != B || d.shape[1] != P * S_loc || d.shape[2] != H_loc || d.shape[3] != D)
-      return fail(LSD_EINVAL, "dst[%d] shape must be (B=%lld, P*S_loc=%lld, H/P=%lld, D=%lld)", t, (long long)B,
-                  (long long)(P * S_loc), (long long)H_loc, (long long)D);
+    if (d.shape[0] != B || d.shape[1] != want1 || d.shape[2] != want2 || d.shape[3] != D)
+      return fail(LSD_EINVAL, "dst[%d] shape must be (B=%lld, %lld, %lld, D=%lld)", t, (long long)B,
+                  (long long)want1, (long long)want2, (long long)D);
   }
   if (B * S_loc * H_loc * D == 0) return ok();
   for (int t = 0; t < n_tensors; ++t) {
@@ -257,7 +282,6 @@ lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_vi
     for (int u = 0; u < t; ++u)
       if (overlaps(sd, span_of(dst[u], 2))) return fail(LSD_EINVAL, "dst[%d] overlaps dst[%d]", t, u);
   }
-  if ((s = check_device()) != LSD_OK) return s;
 
   lsd::RelayoutArgs a;
   std::memset(&a, 0, sizeof a);
@@ -280,7 +304,25 @@ lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_vi
   a.n_tensors = n_tensors; a.P = P; a.rank = rank; a.B = (int)B; a.S_loc = (int)S_loc;
   a.H_loc = (int)H_loc; a.D = (int)D;
   a.heads_per_run = contiguous_heads ? (int)H_loc : 1;
-  return launched(lsd::launch_relayout(a, (hipStream_t)stream), "relayout_seq_to_head");
+  a.inverse = inverse ? 1 : 0;
+  if (lsd::relayout_runs(a) > 0x7fffffff)
+    return fail(LSD_EUNSUPPORTED, "%s: %lld copy runs exceed 2^31-1", fn, (long long)lsd::relayout_runs(a));
+  if ((s = check_device()) != LSD_OK) return s;
+  return launched(lsd::launch_relayout(a, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,
+                                    void* stream) {
+  return relayout(false, "relayout_seq_to_head", n_tensors, P, rank, src, dst, stream);
+}
+
+lsd_status lsd_relayout_head_to_seq(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,
+                                    void* stream) {
+  return relayout(true, "relayout_head_to_seq", n_tensors, P, rank, src, dst, stream);
 }
 
 }  // extern "C"

@@ -71,10 +71,14 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// IEEE maximum: lowers to v_maximum3_f32 without the NaN-quieting copies that
+// fmaxf needs for MFMA results (NaN inputs are outside the contract anyway).
+__device__ inline float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
 __device__ inline float partner_max(float x) {
   // lanes l and l^32 hold the two halves of one query row
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 __device__ inline float partner_sum(float x) {
@@ -134,16 +138,20 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     }
   }
 
-  // ---- global -> register -> LDS staging.  Rows past S_kv are read from the
-  // last valid row instead (finite data, no branch): their scores are masked
-  // to -inf, so they get zero weight.
-  const int last_row = a.S_kv - 1;
+  // ---- global -> register -> LDS staging, with buffer loads.  Each tile
+  // gets a buffer descriptor (built in scalar registers) whose base is the
+  // tile's first row and whose byte range ends with the last valid row, so a
+  // lane's offset inside the tile is fixed for the whole kernel and rows past
+  // S_kv read as zero (their scores are masked to -inf, so they get zero
+  // weight).  Tiles past the end get an empty range.
   int k_row[C::kLoadsPerThread], k_ch[C::kLoadsPerThread];
+  uint32_t k_off[C::kLoadsPerThread];
 #pragma unroll
   for (int u = 0; u < C::kLoadsPerThread; ++u) {
     const int idx = tid + kThreads * u;
     k_row[u] = idx / C::kChunksPerRow;
     k_ch[u] = idx % C::kChunksPerRow;
+    k_off[u] = (uint32_t)(k_row[u] * a.k_ss + 8 * k_ch[u]) * 2u;
   }
   // V: thread -> (key pair, 16-byte d-chunk); each wave covers all 32 pairs of
   // a tile for two chunks, which keeps the transposing writes conflict-free.
@@ -151,22 +159,26 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   const int vp_pair = (tid & 63) >> 1;
   const bool v_loader = 2 * (tid >> 6) + (tid & 1) < C::kChunksPerRow;
   const int vp_chunk = v_loader ? 2 * (tid >> 6) + (tid & 1) : 0;
+  const uint32_t v_off0 = (uint32_t)(2 * vp_pair * a.v_ss + 8 * vp_chunk) * 2u;
+  const uint32_t v_off1 = v_off0 + (uint32_t)a.v_ss * 2u;
   u32x4 kst[C::kLoadsPerThread], vst[2];
+  auto tile_bytes = [&](int t, int64_t ss) -> int {
+    const int64_t rows = (int64_t)a.S_kv - (int64_t)t * kBlockN;
+    const int64_t any = -(int64_t)(rows > 0);  // all ones if a row is left
+    const int64_t n = ((min(rows, (int64_t)kBlockN) - 1) * ss * 2 + 2 * D) & any;
+    return (int)n;
+  };
   auto load_k = [&](int t) {
-    const int r0 = t * kBlockN;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)t * kBlockN * a.k_ss), (short)0, tile_bytes(t, a.k_ss), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < C::kLoadsPerThread; ++u) {
-      const int j = min(r0 + k_row[u], last_row);
-      kst[u] = *(const u32x4*)(kbase + (int64_t)j * a.k_ss + 8 * k_ch[u]);
-    }
+    for (int u = 0; u < C::kLoadsPerThread; ++u) kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off[u], 0, 0);
   };
   auto load_v = [&](int t) {
-    const int r0 = t * kBlockN + 2 * vp_pair;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = min(r0 + u, last_row);
-      vst[u] = *(const u32x4*)(vbase + (int64_t)j * a.v_ss + 8 * vp_chunk);
-    }
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)t * kBlockN * a.v_ss), (short)0, tile_bytes(t, a.v_ss), 0x00020000);
+    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
+    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
   };
   auto store_k = [&](int t) {
 #pragma unroll
@@ -215,13 +227,16 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
       }
   };
   auto softmax = [&]() {
-    float mx = __builtin_fmaxf(sacc[0][0], sacc[0][1]);
+    // two chains of 3-input maxima (one instruction per two scores)
+    float mx0 = sacc[0][0], mx1 = sacc[1][0];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[0][r], sacc[0][r + 1]));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[1][r], sacc[1][r + 1]));
+    for (int r = 1; r < 15; r += 2) {
+      mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
+      mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+    }
+    float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
     mx = partner_max(mx) * c;
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = vmax(m_run, mx);
     const bool need = m_new > m_run + kRescaleThreshold;
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -309,8 +324,8 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // their chunks of K_{t+2} and V_{t+1} during their G(t) (intervals 2t+1 and
   // 2t+2), after every reader of those buffers has passed a barrier, and issue
   // the global loads of K_{t+3} and V_{t+2}, in flight for one iteration.  Past
-  // the last tile these reads and writes touch stale buffers (clamped global
-  // addresses) whose results are never used.
+  // the last tile the loads have an empty range (they return zero) and the LDS
+  // writes fill buffers whose contents are never used.
   const int group = wave >> 2;
   load_k(0);
   load_v(0);

@@ -48,7 +48,14 @@ struct RelayoutArgs {
   int64_t dst_sb[kMaxRelayoutTensors], dst_ss[kMaxRelayoutTensors], dst_sh[kMaxRelayoutTensors];
   int n_tensors, P, rank, B, S_loc, H_loc, D;
   int heads_per_run;  // H_loc when every head slice is contiguous in src and dst, else 1
+  // 0: sequence-major shards -> head-major slice (src[t][p] is shard p of the
+  //    sequence, (B, S_loc, H, D); dst[t] is (B, P*S_loc, H_loc, D)).
+  // 1: the inverse, head-major slices -> sequence shard (src[t][r] is rank
+  //    r's slice, (B, P*S_loc, H_loc, D); dst[t] is (B, S_loc, P*H_loc, D)).
+  int inverse;
 };
+// Number of copy runs (one per token, tensor and head group) of a relayout.
+int64_t relayout_runs(const RelayoutArgs& a);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream);
 
 }  // namespace lsd

@@ -1,19 +1,25 @@
-// Ulysses sequence-major -> head-major relayout for one destination rank, gfx950.
+// Ulysses relayouts for one rank, gfx950: sequence-major -> head-major before
+// attention and head-major -> sequence-major after it.
 //
-//   dst[t][b, p*S_loc + s, j, :] = src[t][p][b, s, rank*H_loc + j, :]
+//   forward: dst[t][b, p*S_loc + s, j, :] = src[t][p][b, s, rank*H_loc + j, :]
+//   inverse: dst[t][b, s, r*H_loc + j, :] = src[t][r][b, rank*S_loc + s, j, :]
 //
 // ("Scaling Video Generation Across NVL72 rack with TensorRT-LLM", "Ulysses
-// Parallelism": [B, S/P, H, D] -> [B, S, H/P, D], Q/K/V moved together from the
+// Parallelism" and its Figure 2: [B, S/P, H, D] -> [B, S, H/P, D] before the
+// full-sequence attention and back after it, Q/K/V moved together from the
 // fused projection; "CUDA IPC Ulysses" (TeleFuser), "Strided Copy Engine
 // scatter": the strided V view is read in place and written straight into the
-// final layout.)  A pure copy of 16-bit patterns; no arithmetic.
+// final layout; "How 8 GPUs split tokens" (LTX-2 SP), "Precise statement": the
+// round trip returns every byte.)  A pure copy of 16-bit patterns.
 //
 // HBM-bound stream.  The copy is cut into runs: one run is the H_loc*D
-// contiguous elements one token contributes to one tensor (or one head's D
-// elements when a view's head slices are not contiguous).  Each wave copies
-// whole runs with 16-byte loads and stores; all loads of a run are issued
-// before its stores.  Run indices are wave-uniform, so the per-run address
-// arithmetic (tensor, shard, token) stays in scalar registers.
+// contiguous elements one token contributes to one tensor from one rank's
+// head slice (or one head's D elements when a view's head slices are not
+// contiguous).  Each wave copies whole runs with 16-byte loads and stores; all
+// loads of a run are issued before its stores.  Run indices are wave-uniform,
+// so the per-run address arithmetic (tensor, shard, token) stays in scalar
+// registers, in 32 bits (the host checks the run count).  Runs are numbered so
+// that consecutive runs write consecutive destination bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,28 +34,46 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kUnroll = 4;  // 16-byte vectors per lane in flight per pass
 
-__global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a, int64_t n_runs) {
+template <bool kInverse>
+__global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a, int n_runs) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = a.P * a.S_loc;
   const int runs_per_token = a.H_loc / a.heads_per_run;
   const int vpr = a.heads_per_run * a.D / 8;  // vectors per run
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  const int stride = (int)gridDim.x * kWavesPerBlock;
 
-  for (int64_t run = (int64_t)blockIdx.x * kWavesPerBlock + wave; run < n_runs; run += stride) {
-    const int jr = (int)(run % runs_per_token);
-    const int64_t tok = run / runs_per_token;
-    const int sg = (int)(tok % S);
-    const int64_t tb = tok / S;
-    const int b = (int)(tb % a.B);
-    const int t = (int)(tb / a.B);
-    const int p = sg / a.S_loc;
-    const int s = sg - p * a.S_loc;
+  for (int run = (int)blockIdx.x * kWavesPerBlock + wave; run < n_runs; run += stride) {
+    const int jr = run % runs_per_token;
+    const int tok = run / runs_per_token;
     const int j0 = jr * a.heads_per_run;
+    int p, s, tb;
+    if (!kInverse) {  // tok = ((t*B + b)*P + p)*S_loc + s
+      s = tok % a.S_loc;
+      const int tp = tok / a.S_loc;
+      p = tp % a.P;
+      tb = tp / a.P;
+    } else {          // tok = ((t*B + b)*S_loc + s)*P + r, p = source rank r
+      p = tok % a.P;
+      const int ts = tok / a.P;
+      s = ts % a.S_loc;
+      tb = ts / a.S_loc;
+    }
+    const int b = tb % a.B;
+    const int t = tb / a.B;
 
-    const uint16_t* sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)s * a.src_ss[t][p] +
-                         (int64_t)(a.rank * a.H_loc + j0) * a.src_sh[t][p];
-    uint16_t* dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)sg * a.dst_ss[t] + (int64_t)j0 * a.dst_sh[t];
+    const uint16_t* sp;
+    uint16_t* dp;
+    if (!kInverse) {
+      sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)s * a.src_ss[t][p] +
+           (int64_t)(a.rank * a.H_loc + j0) * a.src_sh[t][p];
+      dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)(p * a.S_loc + s) * a.dst_ss[t] +
+           (int64_t)j0 * a.dst_sh[t];
+    } else {
+      sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)(a.rank * a.S_loc + s) * a.src_ss[t][p] +
+           (int64_t)j0 * a.src_sh[t][p];
+      dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)s * a.dst_ss[t] +
+           (int64_t)(p * a.H_loc + j0) * a.dst_sh[t];
+    }
 
     for (int v0 = 0; v0 < vpr; v0 += 64 * kUnroll) {
       u32x4 buf[kUnroll];
@@ -69,14 +93,22 @@ __global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a
 
 }  // namespace
 
+int64_t relayout_runs(const RelayoutArgs& a) {
+  return (int64_t)a.n_tensors * a.B * a.P * a.S_loc * (a.H_loc / a.heads_per_run);
+}
+
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream) {
-  const int64_t n_runs = (int64_t)a.n_tensors * a.B * a.P * a.S_loc * (a.H_loc / a.heads_per_run);
+  const int64_t n_runs = relayout_runs(a);
   if (n_runs == 0) return hipSuccess;
+  if (n_runs > 0x7fffffff) return hipErrorInvalidValue;
   // enough waves to cover the chip several times; each wave loops over runs
   int64_t blocks = (n_runs + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t cap = 256 * 8 * 4;  // CUs x (workgroups per CU in flight) x passes
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, n_runs);
+  if (a.inverse)
+    hipLaunchKernelGGL(relayout_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, (int)n_runs);
+  else
+    hipLaunchKernelGGL(relayout_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, (int)n_runs);
   return hipGetLastError();
 }
 

@@ -176,6 +176,46 @@ def test_relayout_validation():
     assert r == LSD_EINVAL and "overlaps src" in msg
 
 
+def relayout_inv(nt, P, rank, src, dst):
+    L = lsd.lib()
+    sv = (View4 * len(src))(*src)
+    dv = (View4 * len(dst))(*dst)
+    r = L.lsd_relayout_head_to_seq(nt, P, rank, sv, dv, None)
+    return r, L.lsd_last_error().decode()
+
+
+def test_relayout_head_to_seq_validation():
+    B, S_loc, H_loc, D, P = 2, 50, 10, 128, 4
+    src = [view(BASE + r * GB, (B, P * S_loc, H_loc, D)) for r in range(P)]
+    dst = [view(BASE + 10 * GB, (B, S_loc, P * H_loc, D))]
+    assert relayout_inv(0, P, 0, src, dst)[0] == LSD_EINVAL
+    assert relayout_inv(1, 0, 0, src, dst)[0] == LSD_EINVAL
+    assert relayout_inv(1, 17, 0, src * 5, dst)[0] == LSD_EUNSUPPORTED
+    r, msg = relayout_inv(1, P, -1, src, dst)
+    assert r == LSD_EINVAL and "rank" in msg
+    # the slices' sequence length must split into P equal shards
+    odd = [view(BASE + r * GB, (B, P * S_loc + 1, H_loc, D)) for r in range(P)]
+    r, msg = relayout_inv(1, P, 0, odd, dst)
+    assert r == LSD_EINVAL and "not divisible" in msg
+    uneq = list(src)
+    uneq[2] = view(BASE + 2 * GB, (B, P * S_loc, H_loc + 1, D))
+    r, msg = relayout_inv(1, P, 0, uneq, dst)
+    assert r == LSD_EINVAL and "same shape" in msg
+    r, msg = relayout_inv(1, P, 0, src, [view(BASE + 10 * GB, (B, S_loc, H_loc, D))])
+    assert r == LSD_EINVAL and "dst[0] shape" in msg
+    r, msg = relayout_inv(1, P, 0, src, [view(BASE + GB + 4096, (B, S_loc, P * H_loc, D))])
+    assert r == LSD_EINVAL and "overlaps src" in msg
+    r, msg = relayout_inv(2, P, 0, src + src, dst + dst)
+    assert r == LSD_EINVAL and "overlaps" in msg
+
+
+def test_attn_fwd_rejects_huge_kv_stride():
+    q, k, v, o = good4()
+    k = view(BASE + GB, (1, 256, 2, 64), [256 * (1 << 24), 1 << 24, 64, 1])
+    r, msg = attn(q, k, v, o)
+    assert r == LSD_EUNSUPPORTED and "2^24" in msg
+
+
 def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)

@@ -79,6 +79,19 @@ def test_wan_ulysses_share_relayout_then_attention():
         del qkv, o, lse
 
 
+def test_wan_inverse_relayout_full_size():
+    note("full Wan inverse relayout: 4 rank slices [2,75600,10,128] -> shard [2,18900,40,128]")
+    t = torch()
+    B, S, H_loc, D, P = 2, 75_600, 10, 128, 4
+    host = [synth.random_bits16((B, S, H_loc, D), 900 + r) for r in range(P)]
+    dev = [to_dev(x) for x in host]
+    for p in (0, 3):
+        out = lsd.relayout_head_to_seq([dev], P, p)[0]
+        t.cuda.synchronize()
+        assert np.array_equal(to_bits(out), ref.relayout_head_to_seq(host, P, p)), f"shard {p}"
+        del out
+
+
 def test_ring_share_blocks_and_merge():
     note("full Ring/Attention2D share: Q 25200 x 3 K/V blocks of 25200, H=40")
     t = torch()

@@ -1,5 +1,6 @@
-"""relayout_seq_to_head on the GPU (through the C ABI): bit-exact against the
-oracle on random 16-bit patterns (NaN payloads, infinities and -0 included)."""
+"""relayout_seq_to_head and relayout_head_to_seq on the GPU (through the C
+ABI): bit-exact against the oracle on random 16-bit patterns (NaN payloads,
+infinities and -0 included), and the GPU round trip returns every byte."""
 
 import numpy as np
 import pytest
@@ -75,3 +76,52 @@ def test_round_trip_byte_exact():
     t.cuda.synchronize()
     for p in range(P):
         assert np.array_equal(ref.relayout_head_to_seq(ys, P, p), host[p])
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("n_tensors", [1, 3])
+def test_inverse_all_ranks_bit_exact(P, n_tensors):
+    note(f"relayout_head_to_seq P={P} n_tensors={n_tensors}")
+    t = torch()
+    B, S_loc, H_loc, D = 2, 23, 3, 128
+    host = [[synth.random_bits16((B, P * S_loc, H_loc, D), 5000 + 1000 * tt + 10 * P + r) for r in range(P)]
+            for tt in range(n_tensors)]
+    dev = [[to_dev(x) for x in row] for row in host]
+    for p in range(P):
+        outs = lsd.relayout_head_to_seq(dev, P, p)
+        t.cuda.synchronize()
+        for tt in range(n_tensors):
+            assert outs[tt].shape == (B, S_loc, P * H_loc, D)
+            assert np.array_equal(to_bits(outs[tt]), ref.relayout_head_to_seq(host[tt], P, p))
+
+
+def test_gpu_round_trip_byte_exact():
+    note("relayout seq->head->seq on the GPU, every rank")
+    t = torch()
+    B, S_loc, H, D, P = 2, 41, 8, 64, 4
+    host = [synth.random_bits16((B, S_loc, H, D), 600 + p) for p in range(P)]
+    dev = [to_dev(x) for x in host]
+    ys = [lsd.relayout_seq_to_head([dev], P, r)[0] for r in range(P)]
+    back = [lsd.relayout_head_to_seq([ys], P, p)[0] for p in range(P)]
+    t.cuda.synchronize()
+    for p in range(P):
+        assert np.array_equal(to_bits(back[p]), host[p])
+
+
+def test_inverse_strided_views_and_guard_bands():
+    note("relayout_head_to_seq strided source + head-strided destination + guard bands")
+    t = torch()
+    B, S_loc, H_loc, D, P = 1, 17, 2, 64, 3
+    # rank slices are views into one wider buffer (every other head slot)
+    wide = [to_dev(synth.random_bits16((B, P * S_loc, 2 * H_loc, D), 700 + r)) for r in range(P)]
+    src = [w[:, :, ::2] for w in wide]
+    host_src = [to_bits(x) for x in src]
+    sentinel = -777
+    big = t.full((B, S_loc, 2 * P * H_loc + 2, D), sentinel, dtype=t.int16, device="cuda")
+    dst = big.view(t.bfloat16)[:, :, 1:1 + 2 * P * H_loc:2]
+    lsd.relayout_head_to_seq([src], P, 2, dst=[dst])
+    t.cuda.synchronize()
+    assert np.array_equal(to_bits(dst), ref.relayout_head_to_seq(host_src, P, 2))
+    bb = big.cpu().numpy()
+    assert (bb[:, :, 0] == sentinel).all() and (bb[:, :, 2:2 * P * H_loc + 1:2] == sentinel).all()
+    assert (bb[:, :, -1] == sentinel).all()
