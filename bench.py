@@ -50,6 +50,10 @@ WORKLOADS = {
                 D=128, P=4, kv_blocks=1, seed=2),
     "ring": dict(desc="Ring/Attention2D share: Q [1,25200,40,128] vs 3 K/V blocks of 25200 with fp32 LSE "
                       "-> LSE merge (n=3)", B=1, S=25_200, H=40, D=128, P=None, kv_blocks=3, seed=3),
+    "ring_stream": dict(desc="Ring share with the merge folded into attention: Q [1,25200,40,128] vs 3 K/V "
+                             "blocks of 25200, each step attn_fwd_accumulate into a running fp32 (O, LSE); the "
+                             "last step also writes bf16 O", B=1, S=25_200, H=40, D=128, P=None, kv_blocks=3,
+                        seed=3, stream=True),
     "cosmos": dict(desc="Cosmos3-Super share: Q,K,V [1,150000,16,128], 1% of keys x4, with fp32 LSE", B=1,
                    S=150_000, H=16, D=128, P=None, kv_blocks=1, seed=4),
     "tiny": dict(desc="tiny: fused QKV [1,256,3,2,64] -> relayout (P=1) -> attention over 4 K/V chunks -> merge",
@@ -103,7 +107,7 @@ class Pipeline:
             hl = H // P
             self.qkv = [torch.empty((B, S, hl, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
             self.Hq = hl
-        elif name == "ring":
+        elif name in ("ring", "ring_stream"):
             q, k, v = synth.qkv(B, S, 3 * S, H, D, seed=w["seed"])
             self.host.update(q=q, k=k, v=v)
             self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
@@ -124,7 +128,12 @@ class Pipeline:
             self.o = torch.empty((B, self.S_q, Hq, D), dtype=torch.bfloat16, device="cuda")
             self.lse = torch.empty((B, Hq, self.S_q), dtype=torch.float32, device="cuda")
         self.has_relayout = name in ("ltx2", "tiny", "wan")
-        self.has_merge = nb > 1
+        self.stream = bool(w.get("stream"))
+        self.has_merge = nb > 1 and not self.stream
+        if self.stream:
+            self.o_acc = torch.empty((B, self.S_q, Hq, D), dtype=torch.float32, device="cuda")
+            self.lse_acc = torch.empty((B, Hq, self.S_q), dtype=torch.float32, device="cuda")
+            self.o = torch.empty((B, self.S_q, Hq, D), dtype=torch.bfloat16, device="cuda")
         # Ulysses output side: with P > 1 the attention output goes back to
         # sequence shard 0; the other ranks' head slices are seeded stand-ins.
         self.has_inverse = self.has_relayout and w["P"] > 1
@@ -164,9 +173,16 @@ class Pipeline:
             lsd.relayout_seq_to_head(self.src, self.w["P"], 0, dst=self.qkv)
             mark()
         q, kk, v = self.qkv
+        if self.stream:
+            self.lse_acc.fill_(float("-inf"))          # no history yet
         for i, (lo, hi) in enumerate(self.bounds):
             mark()
-            lsd.attn_fwd(q, kk[:, lo:hi], v[:, lo:hi], o=self.o_parts[i], lse=self.lse_parts[i])
+            if self.stream:
+                last = i == len(self.bounds) - 1
+                lsd.attn_fwd_accumulate(q, kk[:, lo:hi], v[:, lo:hi], self.o_acc, self.lse_acc,
+                                        o=self.o if last else None)
+            else:
+                lsd.attn_fwd(q, kk[:, lo:hi], v[:, lo:hi], o=self.o_parts[i], lse=self.lse_parts[i])
             mark()
         if self.has_merge:
             mark()
@@ -377,7 +393,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w["desc"], "B": w["B"], "S_q": pipe.S_q, "S_kv": pipe.S_kv, "H": pipe.Hq,
-                   "D": w["D"], "kv_blocks": w["kv_blocks"], "flop_per_step": pipe.flops},
+                   "D": w["D"], "kv_blocks": w["kv_blocks"], "fused_merge": pipe.stream,
+                   "flop_per_step": pipe.flops},
         "roofline": {"bound": "mfma", "achieved": round(flops_per_launch / (attn_ms * 1e-3) / 1e12, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops_per_launch / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -1,11 +1,13 @@
 /*
  * lsd.h - C ABI of the long-sequence DiT attention library (MI355X, gfx950).
  *
- * Four calls make up the hot path of one sequence-parallel DiT attention
+ * These calls make up the hot path of one sequence-parallel DiT attention
  * layer on one GPU:
  *
  *   lsd_relayout_seq_to_head  seq-major shards -> head-major slice (Ulysses)
  *   lsd_attn_fwd              dense bidirectional attention, O and optional LSE
+ *   lsd_attn_fwd_accumulate   the same against one K/V block, merged in place
+ *                             into a running (O, LSE) (Ring step)
  *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
  *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
  *                             after attention)
@@ -91,6 +93,36 @@ const char* lsd_last_error(void);
  */
 lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
                         const lsd_view4* o, float* lse, float softmax_scale, void* stream);
+
+/*
+ * One Ring step with the merge folded in: attention of q against one key/value
+ * block, merged into a running result in place.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+ * "Context Parallelism > Ring Attention" (each arriving K/V block's partial
+ * result is merged into the running output with the fp32 online-softmax
+ * recurrence, so no separate combine pass is needed) and "Limitations and
+ * Future Work" (folding the combine into the attention kernel).
+ *
+ *   q, k, v  as for lsd_attn_fwd (k, v: this step's key/value block)
+ *   o_acc    float32 [B, S_q, H, D] contiguous, 16-byte aligned: read, written
+ *   lse_acc  float32 [B, H, S_q] contiguous: read, written
+ *   o        (B, S_q, H, D) bf16, written if non-NULL: the updated running
+ *            output rounded to bf16 (pass it on the last step)
+ *
+ * With (O_b, LSE_b) this block's attention result (as lsd_attn_fwd computes
+ * it, kept in float32), M = max(LSE_acc, LSE_b) and w = exp(LSE - M):
+ *   O_acc   <- (w_acc O_acc + w_b O_b) / (w_acc + w_b)
+ *   LSE_acc <- M + ln(w_acc + w_b)
+ * Start a sequence of steps with lse_acc = -inf: where LSE_acc = -inf the
+ * running O_acc is not read (it may hold anything).  A block with no keys
+ * (S_kv == 0) leaves o_acc and lse_acc unchanged (and writes their bf16 form,
+ * 0 where LSE_acc = -inf, to o).  lse_acc must hold LSEs or -inf (no NaN).
+ * Other rules as for lsd_attn_fwd; o_acc, lse_acc and o may not overlap each
+ * other or an input.
+ */
+lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, float* o_acc,
+                                   float* lse_acc, const lsd_view4* o, float softmax_scale, void* stream);
 
 /*
  * Exact merge of n partial attention results over disjoint key spans.

@@ -53,6 +53,9 @@ def lib():
         L.lsd_relayout_seq_to_head.restype = ctypes.c_int
         L.lsd_relayout_seq_to_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
+        L.lsd_attn_fwd_accumulate.restype = ctypes.c_int
+        L.lsd_attn_fwd_accumulate.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
+                                              P(View4), ctypes.c_float, ctypes.c_void_p]
         L.lsd_relayout_head_to_seq.restype = ctypes.c_int
         L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
@@ -129,6 +132,25 @@ def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_ls
                             ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q))
     _check(st, "lsd_attn_fwd")
     return (o, lse) if lse is not None else o
+
+
+def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, o=None, scale=None):
+    """One Ring step: attention of q against the key/value block (k, v), merged
+    in place into the running float32 result o_acc [B,S_q,H,D] and lse_acc
+    [B,H,S_q] (start with lse_acc = -inf).  If ``o`` (bf16 [B,S_q,H,D]) is given,
+    the updated running output is also written to it in bf16.  Returns o."""
+    B, S_q, H, D = q.shape
+    qv, kv, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
+    ov = _view(o, "o") if o is not None else None
+    if o_acc is None or lse_acc is None:
+        raise ValueError("attn_fwd_accumulate: o_acc and lse_acc are required")
+    pa = _f32_ptr(o_acc, "o_acc", (B, S_q, H, D))
+    pl = _f32_ptr(lse_acc, "lse_acc", (B, H, S_q))
+    st = lib().lsd_attn_fwd_accumulate(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pa, pl,
+                                       ctypes.byref(ov) if ov is not None else None,
+                                       ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q))
+    _check(st, "lsd_attn_fwd_accumulate")
+    return o
 
 
 def attn_merge(o_parts: Sequence, lse_parts: Sequence, o=None, lse=None, return_lse: bool = True):

@@ -121,6 +121,75 @@ lsd_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+
+// Shared validation and launch of both attention entry points.  In
+// accumulate mode o (bf16 output) is optional and lse is unused; o_acc
+// ([B,S_q,H,D] fp32) and lse_acc ([B,H,S_q] fp32) are read and written.
+lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const lsd_view4* o,
+                     float* lse, float* o_acc, float* lse_acc, float softmax_scale, void* stream) {
+  lsd_status s;
+  if ((s = check_view("q", q)) != LSD_OK) return s;
+  if ((s = check_view("k", k)) != LSD_OK) return s;
+  if ((s = check_view("v", v)) != LSD_OK) return s;
+  if ((!acc || o != nullptr) && (s = check_view("o", o)) != LSD_OK) return s;
+  const int64_t B = q->shape[0], S_q = q->shape[1], H = q->shape[2], D = q->shape[3];
+  const int64_t S_kv = k->shape[1];
+  if (k->shape[0] != B || k->shape[2] != H || k->shape[3] != D)
+    return fail(LSD_EINVAL, "k shape (%lld,%lld,%lld,%lld) does not match q (B=%lld, H=%lld, D=%lld)",
+                (long long)k->shape[0], (long long)k->shape[1], (long long)k->shape[2], (long long)k->shape[3],
+                (long long)B, (long long)H, (long long)D);
+  if (!same_shape(*v, *k)) return fail(LSD_EINVAL, "v shape must equal k shape (B, S_kv, H, D)");
+  if (o != nullptr && !same_shape(*o, *q)) return fail(LSD_EINVAL, "o shape must equal q shape (B, S_q, H, D)");
+  if (D != 64 && D != 128) return fail(LSD_EUNSUPPORTED, "head dim D=%lld unsupported (64 or 128)", (long long)D);
+  // a 64-key K/V tile is addressed with 32-bit byte offsets
+  if (k->stride[1] >= (int64_t(1) << 24) || v->stride[1] >= (int64_t(1) << 24))
+    return fail(LSD_EUNSUPPORTED, "k/v sequence stride (%lld, %lld elements) must be below 2^24",
+                (long long)k->stride[1], (long long)v->stride[1]);
+  if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
+  if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
+  if (acc) {
+    if (o_acc == nullptr || lse_acc == nullptr) return fail(LSD_EINVAL, "null o_acc or lse_acc");
+    if ((uintptr_t)o_acc % 16 != 0) return fail(LSD_EINVAL, "o_acc not 16-byte aligned");
+    if ((uintptr_t)lse_acc % 4 != 0) return fail(LSD_EINVAL, "lse_acc not 4-byte aligned");
+  }
+  if (B * S_q * H == 0) return ok();
+
+  const Span sq = span_of(*q, 2), sk = span_of(*k, 2), sv = span_of(*v, 2);
+  const Span none = span_flat(nullptr, 0, 1);
+  const Span so = o != nullptr ? span_of(*o, 2) : none;
+  const Span sl = span_flat(lse, B * H * S_q, 4);
+  const Span soa = span_flat(o_acc, B * S_q * H * D, 4);
+  const Span sla = span_flat(lse_acc, B * H * S_q, 4);
+  const Span ins[3] = {sq, sk, sv};
+  const Span outs[4] = {so, sl, soa, sla};
+  const char* names[4] = {"o", "lse", "o_acc", "lse_acc"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps an input (q, k or v)", names[i]);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", names[i], names[j]);
+  }
+  if ((s = check_device()) != LSD_OK) return s;
+
+  const float scale = (softmax_scale > 0.0f) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  lsd::AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q->data;
+  a.k = (const uint16_t*)k->data;
+  a.v = (const uint16_t*)v->data;
+  a.o = o != nullptr ? (uint16_t*)o->data : nullptr;
+  a.lse = lse;
+  a.o_acc = o_acc;
+  a.lse_acc = lse_acc;
+  a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
+  if (o != nullptr) { a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2]; }
+  a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv; a.D = (int)D;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), acc ? "attn_fwd_accumulate" : "attn_fwd");
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,51 +200,12 @@ const char* lsd_last_error(void) { return g_err.c_str(); }
 
 lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const lsd_view4* o,
                         float* lse, float softmax_scale, void* stream) {
-  lsd_status s;
-  if ((s = check_view("q", q)) != LSD_OK) return s;
-  if ((s = check_view("k", k)) != LSD_OK) return s;
-  if ((s = check_view("v", v)) != LSD_OK) return s;
-  if ((s = check_view("o", o)) != LSD_OK) return s;
-  const int64_t B = q->shape[0], S_q = q->shape[1], H = q->shape[2], D = q->shape[3];
-  const int64_t S_kv = k->shape[1];
-  if (k->shape[0] != B || k->shape[2] != H || k->shape[3] != D)
-    return fail(LSD_EINVAL, "k shape (%lld,%lld,%lld,%lld) does not match q (B=%lld, H=%lld, D=%lld)",
-                (long long)k->shape[0], (long long)k->shape[1], (long long)k->shape[2], (long long)k->shape[3],
-                (long long)B, (long long)H, (long long)D);
-  if (!same_shape(*v, *k)) return fail(LSD_EINVAL, "v shape must equal k shape (B, S_kv, H, D)");
-  if (!same_shape(*o, *q)) return fail(LSD_EINVAL, "o shape must equal q shape (B, S_q, H, D)");
-  if (D != 64 && D != 128) return fail(LSD_EUNSUPPORTED, "head dim D=%lld unsupported (64 or 128)", (long long)D);
-  // a 64-key K/V tile is addressed with 32-bit byte offsets
-  if (k->stride[1] >= (int64_t(1) << 24) || v->stride[1] >= (int64_t(1) << 24))
-    return fail(LSD_EUNSUPPORTED, "k/v sequence stride (%lld, %lld elements) must be below 2^24",
-                (long long)k->stride[1], (long long)v->stride[1]);
-  if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
-  if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
-  if (B * S_q * H == 0) return ok();
+  return attention(false, q, k, v, o, lse, nullptr, nullptr, softmax_scale, stream);
+}
 
-  const Span so = span_of(*o, 2);
-  const Span sl = span_flat(lse, B * H * S_q, 4);
-  const Span sq = span_of(*q, 2), sk = span_of(*k, 2), sv = span_of(*v, 2);
-  if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv))
-    return fail(LSD_EINVAL, "o overlaps an input (q, k or v)");
-  if (overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv) || overlaps(sl, so))
-    return fail(LSD_EINVAL, "lse overlaps o or an input");
-  if ((s = check_device()) != LSD_OK) return s;
-
-  const float scale = (softmax_scale > 0.0f) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
-  lsd::AttnArgs a;
-  a.q = (const uint16_t*)q->data;
-  a.k = (const uint16_t*)k->data;
-  a.v = (const uint16_t*)v->data;
-  a.o = (uint16_t*)o->data;
-  a.lse = lse;
-  a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
-  a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
-  a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
-  a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2];
-  a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv; a.D = (int)D;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd");
+lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, float* o_acc,
+                                   float* lse_acc, const lsd_view4* o, float softmax_scale, void* stream) {
+  return attention(true, q, k, v, o, nullptr, o_acc, lse_acc, softmax_scale, stream);
 }
 
 lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* lse_parts, const lsd_view4* o_out,

@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -94,7 +95,9 @@ __device__ __host__ constexpr int vt_pos(int j) {
   return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j & 15) >> 3) + (j & 3);
 }
 
-template <int D>
+// kAcc: accumulate mode - this block's result is merged into the running
+// (o_acc, lse_acc) in the epilogue (the Ring step's update, done in place).
+template <int D, bool kAcc>
 __global__ void __launch_bounds__(kThreads)
 attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   using C = Cfg<D>;
@@ -363,6 +366,44 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l)
   const float l_tot = partner_sum(l_run);
   const float inv = 1.0f / l_tot;
+  constexpr float kLn2 = 0.69314718055994530942f;
+  float osc = inv;  // scale from oacc to the output values
+  if constexpr (kAcc) {
+    // Merge with the running result of earlier key blocks (exact LSE merge,
+    // fp32): with M = max(LSE_acc, LSE_blk) and w = exp(LSE - M),
+    //   O_acc <- (w_acc O_acc + w_blk O_blk) / (w_acc + w_blk),
+    //   LSE_acc <- M + ln(w_acc + w_blk).
+    // LSE_blk is finite (the block has keys), so M is; rows with no history
+    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.  Each lane
+    // reads and writes its row's 16-byte runs of O_acc in the accumulator
+    // layout (channels 32 db + 8 g + 4 hh .. +3).
+    const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + qrow;
+    const float lse_b = (m_run + __log2f(l_tot)) * kLn2;
+    const float lse_a = qvalid ? a.lse_acc[lrow] : -INFINITY;
+    const float mx = fmaxf(lse_a, lse_b);
+    const float wa = expf(lse_a - mx);
+    const float wb = expf(lse_b - mx);
+    const float rs = 1.0f / (wa + wb);
+    const float ca = wa * rs, cb = wb * rs * inv;
+    float* orow = a.o_acc + (((int64_t)b * a.S_q + qrow) * a.H + h) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 prev = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (qvalid && wa > 0.0f) prev = *(const f32x4*)(orow + 32 * db + 8 * g);
+        f32x4 nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nv[e] = prev[e] * ca + oacc[db][4 * g + e] * cb;
+          oacc[db][4 * g + e] = nv[e];
+        }
+        if (qvalid) *(f32x4*)(orow + 32 * db + 8 * g) = nv;
+      }
+    if (hh == 0 && qvalid) a.lse_acc[lrow] = mx + logf(wa + wb);
+    osc = 1.0f;
+    if (a.o == nullptr) return;  // uniform: no bf16 output requested
+  }
   // Stage this wave's 32 x D output tile through LDS (the K/V buffers are free
   // once every wave has left the loop) so that global stores write whole
   // 256-byte rows instead of 8-byte pieces of 32 different rows.
@@ -373,12 +414,12 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                 pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+      u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * osc, oacc[db][4 * g + 1] * osc),
+                 pack_bf16(oacc[db][4 * g + 2] * osc, oacc[db][4 * g + 3] * osc)};
       *(u32x2*)(Ow + l32 * kRowO + 32 * db + 8 * g + 4 * hh) = w;
     }
-  if (a.lse != nullptr && hh == 0 && qvalid)
-    a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  if (!kAcc && a.lse != nullptr && hh == 0 && qvalid)
+    a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   // rows are written by 64 lanes: lane = (row r in 0..64/CPR-1, 16-B chunk)
   constexpr int kCPR = D / 8;  // 16-byte chunks per row
   constexpr int kRowsPerPass = 64 / kCPR;
@@ -395,6 +436,8 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
 }
 
 // S_kv == 0: no keys, O = 0 and LSE = -inf (one thread per 8 output elements).
+// In accumulate mode the running result is unchanged and O, if requested, is
+// that running result in bf16 (0 where there is none yet).
 __global__ void attn_empty_kernel(const AttnArgs a) {
   const int64_t rows = (int64_t)a.B * a.S_q * a.H;
   const int vecs = a.D / 8;
@@ -406,8 +449,19 @@ __global__ void attn_empty_kernel(const AttnArgs a) {
     const int64_t bs = row / a.H;
     const int s = (int)(bs % a.S_q);
     const int b = (int)(bs / a.S_q);
-    *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = (u32x4){0u, 0u, 0u, 0u};
-    if (a.lse != nullptr && c == 0) a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (a.o_acc != nullptr) {
+      if (a.o == nullptr) continue;
+      if (a.lse_acc[((int64_t)b * a.H + h) * a.S_q + s] != -INFINITY) {
+        const f32x4* src = (const f32x4*)(a.o_acc + row * a.D + 8 * c);
+        const f32x4 x0 = src[0], x1 = src[1];
+        out = (u32x4){pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]), pack_bf16(x1[0], x1[1]),
+                      pack_bf16(x1[2], x1[3])};
+      }
+    } else if (a.lse != nullptr && c == 0) {
+      a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
+    }
+    *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = out;
   }
 }
 
@@ -416,7 +470,10 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
   const int64_t nblk = (int64_t)n_qtiles * a.H * a.B;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+  if (a.o_acc != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
   return hipGetLastError();
 }
 

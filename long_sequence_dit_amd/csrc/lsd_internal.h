@@ -12,8 +12,12 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  uint16_t* o;
-  float* lse;  // [B, H, S_q] contiguous, may be null
+  uint16_t* o;        // may be null in accumulate mode
+  float* lse;         // [B, H, S_q] contiguous, may be null
+  // Accumulate mode (both non-null): the running result of earlier key
+  // blocks, read and replaced by its merge with this block's result.
+  float* o_acc;       // [B, S_q, H, D] fp32 contiguous
+  float* lse_acc;     // [B, H, S_q] fp32 contiguous
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;

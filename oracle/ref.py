@@ -1,4 +1,5 @@
-"""Float64 CPU oracle: attention with LSE, LSE merge, seq->head relayout.
+"""Float64 CPU oracle: attention with LSE, LSE merge (batched and folded into a
+Ring step), and the Ulysses relayouts in both directions.
 
 Test infrastructure only (see the package docstring): nothing on the product
 path may import it.
@@ -152,6 +153,38 @@ def merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     den = np.transpose(np.where(empty, 1.0, wsum), (0, 2, 1))[..., None]
     O = num / den
     return O, lse
+
+
+def attention_accumulate(o_acc, lse_acc, q, k, v, scale=None):
+    """One Ring step with the merge folded in: the attention result of q
+    against this key/value block, merged into the running result (O_acc,
+    LSE_acc) of earlier blocks.  Where LSE_acc = -inf there is no history and
+    O_acc is ignored (it may hold anything, NaN included).
+
+    o_acc [B, S_q, H, D] floats, lse_acc [B, H, S_q]; q, k, v as for
+    ``attention``.  Returns the new (O, LSE), float64.
+    [NVL72, Ring Attention (each step's partial output is merged into the
+    running result with the online-softmax recurrence); Limitations and
+    Future Work (the combine folded into the attention kernel)]
+    """
+    O_b, L_b = attention(q, k, v, scale)
+    L_a = np.asarray(lse_acc, dtype=np.float64)
+    none = np.transpose(np.isneginf(L_a), (0, 2, 1))[..., None]         # [B,S,H,1]
+    O_a = np.where(none, 0.0, np.asarray(o_acc, dtype=np.float64))
+    return merge([O_a, O_b], [L_a, L_b])
+
+
+def attention_accumulate_rows(o_acc_rows, lse_acc_rows, q, k, v, b: int, h: int, rows: Iterable[int],
+                              scale=None):
+    """``attention_accumulate`` for selected query rows of one (batch, head):
+    o_acc_rows [n, D] and lse_acc_rows [n] are the running result of those
+    rows.  Returns (O [n, D], LSE [n]) float64."""
+    O_b, L_b = attention_rows(q, k, v, b, h, rows, scale)
+    L_a = np.asarray(lse_acc_rows, dtype=np.float64)
+    O_a = np.where(np.isneginf(L_a)[:, None], 0.0, np.asarray(o_acc_rows, dtype=np.float64))
+    n, D = O_b.shape
+    O, L = merge([O_a.reshape(1, n, 1, D), O_b.reshape(1, n, 1, D)], [L_a.reshape(1, 1, n), L_b.reshape(1, 1, n)])
+    return O.reshape(n, D), L.reshape(n)
 
 
 def _logsigmoid(x: np.ndarray) -> np.ndarray:

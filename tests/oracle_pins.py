@@ -289,6 +289,61 @@ def pin_ring_streaming_merge():
     assert np.all(o == 0) and np.all(np.isneginf(l))
 
 
+def pin_accumulate_streams_to_full():
+    """Ring steps with the merge folded in, over disjoint key blocks (one of
+    them empty), starting from no history (LSE = -inf, O = NaN garbage), end
+    at full attention; the rows variant agrees with the full variant."""
+    q, k, v = synth.tiny_qkv()
+    O, L = ref.attention(q, k, v)
+    B, S, H, D = q.shape
+    run_o = np.full((B, S, H, D), np.nan)
+    run_l = np.full((B, H, S), -np.inf)
+    for lo, hi in [(0, 40), (40, 40), (40, 131), (131, 256)]:
+        prev_o, prev_l = run_o, run_l
+        run_o, run_l = ref.attention_accumulate(run_o, run_l, q, k[:, lo:hi], v[:, lo:hi])
+        rows = [0, 7, 255]
+        o_r, l_r = ref.attention_accumulate_rows(prev_o[0, rows, 1], prev_l[0, 1, rows], q, k[:, lo:hi],
+                                                 v[:, lo:hi], 0, 1, rows)
+        assert np.allclose(o_r, run_o[0, rows, 1], rtol=0, atol=1e-13, equal_nan=True)
+        assert np.allclose(l_r, run_l[0, 1, rows], rtol=0, atol=1e-13)
+    assert np.allclose(run_o, O, rtol=0, atol=1e-12) and np.allclose(run_l, L, rtol=0, atol=1e-12)
+    # the ragged, asymmetric case
+    q2 = _rand((2, 13, 3, 64), 33)
+    k2 = _rand((2, 29, 3, 64), 34)
+    v2 = _rand((2, 29, 3, 64), 35)
+    O2, L2 = ref.attention(q2, k2, v2)
+    run_o = np.zeros((2, 13, 3, 64))
+    run_l = np.full((2, 3, 13), -np.inf)
+    for lo, hi in [(0, 1), (1, 17), (17, 29)]:
+        run_o, run_l = ref.attention_accumulate(run_o, run_l, q2, k2[:, lo:hi], v2[:, lo:hi])
+    assert np.allclose(run_o, O2, rtol=0, atol=1e-12) and np.allclose(run_l, L2, rtol=0, atol=1e-12)
+
+
+def pin_accumulate_special_cases():
+    """A block with no keys leaves the running result unchanged (and gives
+    O = 0, LSE = -inf when there is none); with no history the step is plain
+    attention; one step equals the Ring schedule's sigmoid/logsigmoid update
+    of the same two partials."""
+    B, S, H, D = 1, 9, 2, 64
+    q = _rand((B, S, H, D), 36)
+    k = _rand((B, 21, H, D), 37)
+    v = _rand((B, 21, H, D), 38)
+    o_a = _dec(_rand((B, S, H, D), 39))
+    l_a = _dec(_rand((B, H, S), 40)) + 4.0
+    empty_k = k[:, :0]
+    o, l = ref.attention_accumulate(o_a, l_a, q, empty_k, empty_k)
+    assert np.allclose(o, o_a, rtol=0, atol=1e-14) and np.array_equal(l, l_a)
+    ninf = np.full((B, H, S), -np.inf)
+    o, l = ref.attention_accumulate(o_a, ninf, q, empty_k, empty_k)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    Ob, Lb = ref.attention(q, k, v)
+    o, l = ref.attention_accumulate(np.full_like(o_a, np.nan), ninf, q, k, v)
+    assert np.allclose(o, Ob, rtol=0, atol=1e-14) and np.allclose(l, Lb, rtol=0, atol=1e-14)
+    o, l = ref.attention_accumulate(o_a, l_a, q, k, v)
+    o2, l2 = ref.merge_two_logsigmoid(o_a, l_a, Ob, Lb)
+    assert np.allclose(o, o2, rtol=0, atol=1e-12) and np.allclose(l, l2, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------- relayout
 
 def pin_relayout_index_map():
@@ -320,6 +375,21 @@ def pin_relayout_identity_and_round_trip():
             assert np.array_equal(back, chunks[p])
 
 
+def pin_relayout_inverse_index_map():
+    """Element-wise: X_p[b, s, r*H_loc + j, d] = Y_r[b, p*S_loc + s, j, d] for the
+    inverse, by scalar lookups at random positions."""
+    B, S_loc, H_loc, D, P = 2, 6, 3, 16, 4
+    ys = [synth.random_bits16((B, P * S_loc, H_loc, D), 150 + r) for r in range(P)]
+    g = np.random.Generator(np.random.PCG64(10))
+    for p in range(P):
+        x = ref.relayout_head_to_seq(ys, P, p)
+        assert x.shape == (B, S_loc, P * H_loc, D) and x.dtype == np.uint16
+        for _ in range(200):
+            b, r, s = int(g.integers(B)), int(g.integers(P)), int(g.integers(S_loc))
+            j, d = int(g.integers(H_loc)), int(g.integers(D))
+            assert x[b, s, r * H_loc + j, d] == ys[r][b, p * S_loc + s, j, d]
+
+
 def pin_relayout_head_limit():
     """Ulysses degree must divide the head count: with 40 heads on 72 GPUs the
     largest usable degree is 8 (the pages' example)."""
@@ -342,5 +412,7 @@ ATTENTION_PINS = [pin_identical_keys, pin_dominant_logit, pin_rows_sum_to_one, p
                   pin_permutation_and_scaling, pin_scale_argument]
 MERGE_PINS = [pin_merge_equals_full, pin_merge_attention2d_grid, pin_merge_closed_forms,
               pin_ring_streaming_merge]
-RELAYOUT_PINS = [pin_relayout_index_map, pin_relayout_identity_and_round_trip, pin_relayout_head_limit]
-ALL_PINS = ATTENTION_PINS + MERGE_PINS + RELAYOUT_PINS
+ACCUMULATE_PINS = [pin_accumulate_streams_to_full, pin_accumulate_special_cases]
+RELAYOUT_PINS = [pin_relayout_index_map, pin_relayout_identity_and_round_trip, pin_relayout_head_limit,
+                 pin_relayout_inverse_index_map]
+ALL_PINS = ATTENTION_PINS + MERGE_PINS + ACCUMULATE_PINS + RELAYOUT_PINS

@@ -114,6 +114,23 @@ def test_ring_share_blocks_and_merge():
     assert_attention_close(to_f64(om[:, rows]), Om, lm[:, :, rows].cpu().numpy(), Lm, "merge slab")
 
 
+def test_ring_share_streaming_accumulate():
+    note("full Ring share, fused streaming merge: Q [1,25200,40,128] vs 3 K/V blocks of 25200")
+    t = torch()
+    S = 25_200
+    q, k, v = synth.qkv(1, S, 3 * S, 40, 128, seed=3)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    o_acc = t.empty((1, S, 40, 128), dtype=t.float32, device="cuda")
+    lse_acc = t.full((1, 40, S), float("-inf"), dtype=t.float32, device="cuda")
+    o = t.empty((1, S, 40, 128), dtype=t.bfloat16, device="cuda")
+    for i in range(3):
+        note(f"  step {i}")
+        lsd.attn_fwd_accumulate(dq, dk[:, i * S:(i + 1) * S], dv[:, i * S:(i + 1) * S], o_acc, lse_acc,
+                                o=o if i == 2 else None)
+    t.cuda.synchronize()
+    check_rows(o, lse_acc, q, k, v, range(40), 40, "Ring streaming")
+
+
 def test_cosmos_long_sequence_with_outlier_keys():
     note("full Cosmos3-Super share: B=1 S=150000 H=16 D=128, 1% keys x4")
     t = torch()

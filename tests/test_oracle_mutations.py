@@ -163,3 +163,57 @@ RELAYOUT_MUTANTS = [_relayout_next_rank, _relayout_reversed_chunks, _relayout_no
 def test_relayout_mutant_is_caught(monkeypatch, mutant):
     monkeypatch.setattr(ref, "relayout_seq_to_head", mutant)
     assert _run(pins.RELAYOUT_PINS), f"{mutant.__name__} passed every relayout pin"
+
+
+_orig_accumulate = ref.attention_accumulate
+
+
+def _acc_keeps_garbage(o_acc, lse_acc, q, k, v, scale=None):
+    # forgets that O_acc is meaningless where there is no history
+    O_b, L_b = ref.attention(q, k, v, scale)
+    return ref.merge([np.asarray(o_acc, dtype=np.float64), O_b], [np.asarray(lse_acc, dtype=np.float64), L_b])
+
+
+def _acc_replaces(o_acc, lse_acc, q, k, v, scale=None):
+    # the running result is overwritten instead of merged
+    O_b, L_b = ref.attention(q, k, v, scale)
+    return O_b, L_b
+
+
+def _acc_unweighted(o_acc, lse_acc, q, k, v, scale=None):
+    # averages the two results instead of weighting by their LSEs
+    O_b, L_b = ref.attention(q, k, v, scale)
+    L_a = np.asarray(lse_acc, dtype=np.float64)
+    none = np.transpose(np.isneginf(L_a), (0, 2, 1))[..., None]
+    O_a = np.where(none, O_b, np.asarray(o_acc, dtype=np.float64))
+    _, L = ref.merge([O_a, O_b], [L_a, L_b])
+    return 0.5 * (O_a + O_b), L
+
+
+ACCUMULATE_MUTANTS = [_acc_keeps_garbage, _acc_replaces, _acc_unweighted]
+
+
+@pytest.mark.parametrize("mutant", ACCUMULATE_MUTANTS, ids=lambda f: f.__name__)
+def test_accumulate_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "attention_accumulate", mutant)
+    assert _run(pins.ACCUMULATE_PINS), f"{mutant.__name__} passed every accumulate pin"
+
+
+_orig_inverse = ref.relayout_head_to_seq
+
+
+def _inverse_next_shard(heads, P, p):
+    return _orig_inverse(heads, P, (p + 1) % P)
+
+
+def _inverse_reversed_ranks(heads, P, p):
+    return _orig_inverse(list(heads)[::-1], P, p)
+
+
+INVERSE_MUTANTS = [_inverse_next_shard, _inverse_reversed_ranks]
+
+
+@pytest.mark.parametrize("mutant", INVERSE_MUTANTS, ids=lambda f: f.__name__)
+def test_inverse_relayout_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "relayout_head_to_seq", mutant)
+    assert _run(pins.RELAYOUT_PINS), f"{mutant.__name__} passed every relayout pin"
