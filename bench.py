@@ -48,6 +48,10 @@ WORKLOADS = {
                      "-> attention [2,75600,10,128] with fp32 LSE -> inverse relayout of O (this rank's slice "
                      "and 3 stand-in slices of the other ranks) -> shard [2,18900,40,128]", B=2, S=75_600, H=40,
                 D=128, P=4, kv_blocks=1, seed=2),
+    "ltx2_varlen": dict(desc="LTX-2 scale, two clips batched with a key-only padding mask: Q,K,V "
+                             "[2,24576,32,128], valid keys per clip [24576, 16384] (padding filled with NaN); "
+                             "FLOPs count valid keys only", B=2, S=24_576, H=32, D=128, P=None, kv_blocks=1,
+                        seed=5, kv_lens=[24_576, 16_384]),
     "ring": dict(desc="Ring/Attention2D share: Q [1,25200,40,128] vs 3 K/V blocks of 25200 with fp32 LSE "
                       "-> LSE merge (n=3)", B=1, S=25_200, H=40, D=128, P=None, kv_blocks=3, seed=3),
     "ring_stream": dict(desc="Ring share with the merge folded into attention: Q [1,25200,40,128] vs 3 K/V "
@@ -112,6 +116,14 @@ class Pipeline:
             self.host.update(q=q, k=k, v=v)
             self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
             self.Hq = H
+        elif name == "ltx2_varlen":
+            q, k, v = synth.qkv(B, S, S, H, D, seed=w["seed"])
+            for b, n in enumerate(w["kv_lens"]):
+                k[b, n:] = 0x7FC1                               # padding: any read would poison O
+                v[b, n:] = 0x7FC1
+            self.host.update(q=q, k=k, v=v)
+            self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
+            self.Hq = H
         else:  # cosmos
             q, k, v, _ = synth.cosmos_qkv(seed=w["seed"], S=S, H=H, D=D)
             self.host.update(q=q, k=k, v=v)
@@ -150,13 +162,20 @@ class Pipeline:
         else:
             self.inverse_bytes = 0
         B_, D_ = B, D
-        self.flops = 4.0 * B_ * Hq * self.S_q * self.S_kv * D_
+        self.kv_lens = w.get("kv_lens")
+        self.kv_lens_dev = (torch.tensor(self.kv_lens, dtype=torch.int32, device="cuda")
+                            if self.kv_lens is not None else None)
+        n_keys = sum(self.kv_lens) if self.kv_lens is not None else B_ * self.S_kv
+        self.flops = 4.0 * Hq * self.S_q * n_keys * D_
         n_rel = 3 * B_ * self.S_q * Hq * D_
         self.relayout_bytes = 2 * 2 * n_rel if self.has_relayout else 0
         o_bytes = 2 * B_ * self.S_q * Hq * D_
         l_bytes = 4 * B_ * Hq * self.S_q
         self.merge_bytes = (nb + 1) * (o_bytes + l_bytes) if self.has_merge else 0
-        self.attn_flops_per_launch = [4.0 * B_ * Hq * self.S_q * (hi - lo) * D_ for lo, hi in self.bounds]
+        if self.kv_lens is not None:
+            self.attn_flops_per_launch = [self.flops]
+        else:
+            self.attn_flops_per_launch = [4.0 * B_ * Hq * self.S_q * (hi - lo) * D_ for lo, hi in self.bounds]
 
     def step(self, ev=None):
         """One pass; if ev is given, record start/end events around each kernel."""
@@ -182,7 +201,8 @@ class Pipeline:
                 lsd.attn_fwd_accumulate(q, kk[:, lo:hi], v[:, lo:hi], self.o_acc, self.lse_acc,
                                         o=self.o if last else None)
             else:
-                lsd.attn_fwd(q, kk[:, lo:hi], v[:, lo:hi], o=self.o_parts[i], lse=self.lse_parts[i])
+                lsd.attn_fwd(q, kk[:, lo:hi], v[:, lo:hi], o=self.o_parts[i], lse=self.lse_parts[i],
+                             kv_lens=self.kv_lens_dev)
             mark()
         if self.has_merge:
             mark()
@@ -265,7 +285,7 @@ def cpu_baseline(pipe, budget_s):
         r0 = int(g.integers(0, max(1, pipe.S_q - 256)))
         rows = np.arange(r0, min(pipe.S_q, r0 + 256))
         t0 = time.perf_counter()
-        ref.attention_rows(q, k, v, b, hh, rows)
+        ref.attention_rows(q, k, v, b, hh, rows, kv_lens=pipe.kv_lens)
         t_attn += time.perf_counter() - t0
         rows_done += rows.size
         i += 1

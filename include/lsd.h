@@ -6,6 +6,7 @@
  *
  *   lsd_relayout_seq_to_head  seq-major shards -> head-major slice (Ulysses)
  *   lsd_attn_fwd              dense bidirectional attention, O and optional LSE
+ *   lsd_attn_fwd_masked       the same with a key-only padding mask
  *   lsd_attn_fwd_accumulate   the same against one K/V block, merged in place
  *                             into a running (O, LSE) (Ring step)
  *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
@@ -95,6 +96,28 @@ lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4*
                         const lsd_view4* o, float* lse, float softmax_scale, void* stream);
 
 /*
+ * lsd_attn_fwd with a key-only padding mask: batch entry b attends only its
+ * first kv_lens[b] keys; the keys after them (padding) get weight exactly 0,
+ * are never read, and may hold anything (NaN included).  Every query row,
+ * padded rows included, attends all valid keys of its batch entry, so no row
+ * is NaN.  A batch entry with kv_lens[b] == 0 gives O = 0 and LSE = -inf.
+ *
+ * Defined by "How 8 GPUs split tokens: what LTX-2's sequence-parallel all2all
+ * moves", "Data flow": the sequence is padded to a multiple of the parallel
+ * degree and a key-only mask (valid keys 1, padding 0, broadcast over batch
+ * and queries) keeps the padding out of attention; padded query rows see all
+ * valid keys.  Per-batch lengths generalise the single mask to a batch of
+ * sequences of different lengths.
+ *
+ *   kv_lens  int32 device array of B entries, 4-byte aligned; values are
+ *            clamped to [0, S_kv] in the kernel (the host cannot read them).
+ *
+ * Everything else as for lsd_attn_fwd.
+ */
+lsd_status lsd_attn_fwd_masked(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const int32_t* kv_lens,
+                               const lsd_view4* o, float* lse, float softmax_scale, void* stream);
+
+/*
  * One Ring step with the merge folded in: attention of q against one key/value
  * block, merged into a running result in place.
  *
@@ -105,6 +128,8 @@ lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4*
  * Future Work" (folding the combine into the attention kernel).
  *
  *   q, k, v  as for lsd_attn_fwd (k, v: this step's key/value block)
+ *   kv_lens  NULL, or the key-only padding mask of lsd_attn_fwd_masked for
+ *            this block (batch entry b uses the block's first kv_lens[b] keys)
  *   o_acc    float32 [B, S_q, H, D] contiguous, 16-byte aligned: read, written
  *   lse_acc  float32 [B, H, S_q] contiguous: read, written
  *   o        (B, S_q, H, D) bf16, written if non-NULL: the updated running
@@ -121,8 +146,9 @@ lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4*
  * Other rules as for lsd_attn_fwd; o_acc, lse_acc and o may not overlap each
  * other or an input.
  */
-lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, float* o_acc,
-                                   float* lse_acc, const lsd_view4* o, float softmax_scale, void* stream);
+lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
+                                   const int32_t* kv_lens, float* o_acc, float* lse_acc, const lsd_view4* o,
+                                   float softmax_scale, void* stream);
 
 /*
  * Exact merge of n partial attention results over disjoint key spans.

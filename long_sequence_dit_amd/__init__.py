@@ -53,9 +53,12 @@ def lib():
         L.lsd_relayout_seq_to_head.restype = ctypes.c_int
         L.lsd_relayout_seq_to_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
+        L.lsd_attn_fwd_masked.restype = ctypes.c_int
+        L.lsd_attn_fwd_masked.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, P(View4),
+                                          ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
         L.lsd_attn_fwd_accumulate.restype = ctypes.c_int
         L.lsd_attn_fwd_accumulate.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
-                                              P(View4), ctypes.c_float, ctypes.c_void_p]
+                                              ctypes.c_void_p, P(View4), ctypes.c_float, ctypes.c_void_p]
         L.lsd_relayout_head_to_seq.restype = ctypes.c_int
         L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
@@ -113,12 +116,24 @@ def _f32_ptr(t, name, shape):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_lse: bool = True):
+def _lens_ptr(kv_lens, B):
+    torch = _torch()
+    if kv_lens is None:
+        return None
+    if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or not kv_lens.is_contiguous() or \
+            tuple(kv_lens.shape) != (B,):
+        raise ValueError(f"kv_lens: expected a contiguous int32 GPU tensor of shape ({B},)")
+    return ctypes.c_void_p(kv_lens.data_ptr())
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_lse: bool = True, kv_lens=None):
     """O = softmax(scale * Q K^T) V per (batch, head), plus the natural-log LSE.
 
     q: (B, S_q, H, D) bf16, k/v: (B, S_kv, H, D) bf16 (strided views allowed,
     last dim contiguous).  Returns ``o`` (and ``lse`` [B, H, S_q] float32 when
-    ``return_lse``).  ``scale`` defaults to 1/sqrt(D).
+    ``return_lse``).  ``scale`` defaults to 1/sqrt(D).  ``kv_lens`` (int32 [B]
+    on the GPU) is a key-only padding mask: batch entry b attends its first
+    kv_lens[b] keys.
     """
     torch = _torch()
     B, S_q, H, D = q.shape
@@ -128,17 +143,24 @@ def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_ls
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
     vq, vk, vv, vo = _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o")
     lp = _f32_ptr(lse, "lse", (B, H, S_q)) if lse is not None else None
-    st = lib().lsd_attn_fwd(ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), ctypes.byref(vo), lp,
-                            ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q))
-    _check(st, "lsd_attn_fwd")
+    sc = ctypes.c_float(0.0 if scale is None else float(scale))
+    if kv_lens is None:
+        st = lib().lsd_attn_fwd(ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), ctypes.byref(vo), lp, sc,
+                                _stream(q))
+        _check(st, "lsd_attn_fwd")
+    else:
+        st = lib().lsd_attn_fwd_masked(ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), _lens_ptr(kv_lens, B),
+                                       ctypes.byref(vo), lp, sc, _stream(q))
+        _check(st, "lsd_attn_fwd_masked")
     return (o, lse) if lse is not None else o
 
 
-def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, o=None, scale=None):
+def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, o=None, scale=None, kv_lens=None):
     """One Ring step: attention of q against the key/value block (k, v), merged
     in place into the running float32 result o_acc [B,S_q,H,D] and lse_acc
     [B,H,S_q] (start with lse_acc = -inf).  If ``o`` (bf16 [B,S_q,H,D]) is given,
-    the updated running output is also written to it in bf16.  Returns o."""
+    the updated running output is also written to it in bf16.  ``kv_lens`` is
+    the block's key-only padding mask as in ``attn_fwd``.  Returns o."""
     B, S_q, H, D = q.shape
     qv, kv, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
     ov = _view(o, "o") if o is not None else None
@@ -146,7 +168,8 @@ def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, o=None, scale=None):
         raise ValueError("attn_fwd_accumulate: o_acc and lse_acc are required")
     pa = _f32_ptr(o_acc, "o_acc", (B, S_q, H, D))
     pl = _f32_ptr(lse_acc, "lse_acc", (B, H, S_q))
-    st = lib().lsd_attn_fwd_accumulate(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pa, pl,
+    st = lib().lsd_attn_fwd_accumulate(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), _lens_ptr(kv_lens, B),
+                                       pa, pl,
                                        ctypes.byref(ov) if ov is not None else None,
                                        ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q))
     _check(st, "lsd_attn_fwd_accumulate")

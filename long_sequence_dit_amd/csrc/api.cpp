@@ -125,8 +125,9 @@ lsd_status launched(hipError_t e, const char* what) {
 // Shared validation and launch of both attention entry points.  In
 // accumulate mode o (bf16 output) is optional and lse is unused; o_acc
 // ([B,S_q,H,D] fp32) and lse_acc ([B,H,S_q] fp32) are read and written.
-lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const lsd_view4* o,
-                     float* lse, float* o_acc, float* lse_acc, float softmax_scale, void* stream) {
+lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const int32_t* kv_lens,
+                     const lsd_view4* o, float* lse, float* o_acc, float* lse_acc, float softmax_scale,
+                     void* stream) {
   lsd_status s;
   if ((s = check_view("q", q)) != LSD_OK) return s;
   if ((s = check_view("k", k)) != LSD_OK) return s;
@@ -147,6 +148,7 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
                 (long long)k->stride[1], (long long)v->stride[1]);
   if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
   if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
+  if (kv_lens != nullptr && (uintptr_t)kv_lens % 4 != 0) return fail(LSD_EINVAL, "kv_lens not 4-byte aligned");
   if (acc) {
     if (o_acc == nullptr || lse_acc == nullptr) return fail(LSD_EINVAL, "null o_acc or lse_acc");
     if ((uintptr_t)o_acc % 16 != 0) return fail(LSD_EINVAL, "o_acc not 16-byte aligned");
@@ -160,12 +162,13 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   const Span sl = span_flat(lse, B * H * S_q, 4);
   const Span soa = span_flat(o_acc, B * S_q * H * D, 4);
   const Span sla = span_flat(lse_acc, B * H * S_q, 4);
-  const Span ins[3] = {sq, sk, sv};
+  const Span skl = span_flat(kv_lens, B, 4);
+  const Span ins[4] = {sq, sk, sv, skl};
   const Span outs[4] = {so, sl, soa, sla};
   const char* names[4] = {"o", "lse", "o_acc", "lse_acc"};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 3; ++j)
-      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps an input (q, k or v)", names[i]);
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps an input (q, k, v or kv_lens)", names[i]);
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", names[i], names[j]);
   }
@@ -181,6 +184,7 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   a.lse = lse;
   a.o_acc = o_acc;
   a.lse_acc = lse_acc;
+  a.kv_lens = kv_lens;
   a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
   a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
   a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
@@ -200,12 +204,19 @@ const char* lsd_last_error(void) { return g_err.c_str(); }
 
 lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const lsd_view4* o,
                         float* lse, float softmax_scale, void* stream) {
-  return attention(false, q, k, v, o, lse, nullptr, nullptr, softmax_scale, stream);
+  return attention(false, q, k, v, nullptr, o, lse, nullptr, nullptr, softmax_scale, stream);
 }
 
-lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, float* o_acc,
-                                   float* lse_acc, const lsd_view4* o, float softmax_scale, void* stream) {
-  return attention(true, q, k, v, o, nullptr, o_acc, lse_acc, softmax_scale, stream);
+lsd_status lsd_attn_fwd_masked(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v, const int32_t* kv_lens,
+                               const lsd_view4* o, float* lse, float softmax_scale, void* stream) {
+  if (kv_lens == nullptr) return fail(LSD_EINVAL, "null kv_lens");
+  return attention(false, q, k, v, kv_lens, o, lse, nullptr, nullptr, softmax_scale, stream);
+}
+
+lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
+                                   const int32_t* kv_lens, float* o_acc, float* lse_acc, const lsd_view4* o,
+                                   float softmax_scale, void* stream) {
+  return attention(true, q, k, v, kv_lens, o, nullptr, o_acc, lse_acc, softmax_scale, stream);
 }
 
 lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* lse_parts, const lsd_view4* o_out,

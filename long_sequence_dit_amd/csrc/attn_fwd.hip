@@ -97,6 +97,27 @@ __device__ __host__ constexpr int vt_pos(int j) {
 
 // kAcc: accumulate mode - this block's result is merged into the running
 // (o_acc, lse_acc) in the epilogue (the Ring step's update, done in place).
+// Output of one query row's 16-byte chunk c when its (b, h) has no keys:
+// O = 0 and LSE = -inf; in accumulate mode the running result is unchanged
+// and O, if requested, is that running result in bf16 (0 where there is none).
+__device__ inline void write_empty(const AttnArgs& a, int b, int s, int h, int c) {
+  const int64_t row = ((int64_t)b * a.S_q + s) * a.H + h;
+  const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + s;
+  u32x4 out = {0u, 0u, 0u, 0u};
+  if (a.o_acc != nullptr) {
+    if (a.o == nullptr) return;
+    if (a.lse_acc[lrow] != -INFINITY) {
+      const f32x4* src = (const f32x4*)(a.o_acc + row * a.D + 8 * c);
+      const f32x4 x0 = src[0], x1 = src[1];
+      out = (u32x4){pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]), pack_bf16(x1[0], x1[1]),
+                    pack_bf16(x1[2], x1[3])};
+    }
+  } else if (a.lse != nullptr && c == 0) {
+    a.lse[lrow] = -INFINITY;
+  }
+  *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = out;
+}
+
 template <int D, bool kAcc>
 __global__ void __launch_bounds__(kThreads)
 attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
@@ -106,16 +127,18 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   uint16_t* Vs = smem + 2 * C::kLdsK;  // [2][D][kRowVT], V transposed
 
   // ---- XCD-aware tile order: dispatch is round-robin over 8 XCDs; give each
-  // XCD a contiguous range of (b, h, q-tile) so its CUs share K/V in L2.
+  // XCD a contiguous range of (h, b, q-tile) so its CUs share K/V in L2.  The
+  // batch index runs fastest, so with per-batch key lengths every XCD gets
+  // the same mix of long and short batch entries.
   const int nblk = gridDim.x;
   const int pid = blockIdx.x;
   const int xcd = pid & 7;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + min(xcd, rem) + (pid >> 3);
   const int qt = logical % n_qtiles;
-  const int bh = logical / n_qtiles;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  const int hb = logical / n_qtiles;
+  const int b = hb % a.B;
+  const int h = hb / a.B;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,9 +146,22 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;  // lane half
 
+  // Valid keys of this batch entry: all S_kv, or the first kv_lens[b] (the
+  // key-only padding mask; clamped to [0, S_kv]).  Keys past skv get zero
+  // weight and are never read.
+  int skv = a.S_kv;
+  if (a.kv_lens != nullptr) skv = min(max(a.kv_lens[b], 0), a.S_kv);
+  if (skv == 0) {  // block-uniform: no keys for this (b, h)
+    for (int i = threadIdx.x; i < kBlockM * (D / 8); i += kThreads) {
+      const int s = qt * kBlockM + i / (D / 8);
+      if (s < a.S_q) write_empty(a, b, s, h, i % (D / 8));
+    }
+    return;
+  }
+
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
-  const int n_tiles = (a.S_kv + kBlockN - 1) / kBlockN;  // >= 1 (S_kv == 0 never gets here)
+  const int n_tiles = (skv + kBlockN - 1) / kBlockN;  // >= 1
 
   // ---- Q rows of this wave, as MFMA B operands (k = head channel).
   const int qrow = qt * kBlockM + wave * 32 + l32;
@@ -145,7 +181,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // gets a buffer descriptor (built in scalar registers) whose base is the
   // tile's first row and whose byte range ends with the last valid row, so a
   // lane's offset inside the tile is fixed for the whole kernel and rows past
-  // S_kv read as zero (their scores are masked to -inf, so they get zero
+  // the valid keys read as zero (their scores are masked to -inf, so they get zero
   // weight).  Tiles past the end get an empty range.
   int k_row[C::kLoadsPerThread], k_ch[C::kLoadsPerThread];
   uint32_t k_off[C::kLoadsPerThread];
@@ -166,7 +202,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   const uint32_t v_off1 = v_off0 + (uint32_t)a.v_ss * 2u;
   u32x4 kst[C::kLoadsPerThread], vst[2];
   auto tile_bytes = [&](int t, int64_t ss) -> int {
-    const int64_t rows = (int64_t)a.S_kv - (int64_t)t * kBlockN;
+    const int64_t rows = (int64_t)skv - (int64_t)t * kBlockN;
     const int64_t any = -(int64_t)(rows > 0);  // all ones if a row is left
     const int64_t n = ((min(rows, (int64_t)kBlockN) - 1) * ss * 2 + 2 * D) & any;
     return (int)n;
@@ -226,7 +262,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (j >= a.S_kv) sacc[kb][r] = -INFINITY;
+        if (j >= skv) sacc[kb][r] = -INFINITY;
       }
   };
   auto softmax = [&]() {
@@ -353,7 +389,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   }
   if (group == 1) lds_barrier();
   for (int t = 0; t < n_tiles; ++t) {
-    if ((t + 1) * kBlockN > a.S_kv) mask_tail(t);
+    if ((t + 1) * kBlockN > skv) mask_tail(t);
     softmax();
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
@@ -435,9 +471,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   }
 }
 
-// S_kv == 0: no keys, O = 0 and LSE = -inf (one thread per 8 output elements).
-// In accumulate mode the running result is unchanged and O, if requested, is
-// that running result in bf16 (0 where there is none yet).
+// S_kv == 0: no keys anywhere (one thread per 8 output elements).
 __global__ void attn_empty_kernel(const AttnArgs a) {
   const int64_t rows = (int64_t)a.B * a.S_q * a.H;
   const int vecs = a.D / 8;
@@ -449,19 +483,7 @@ __global__ void attn_empty_kernel(const AttnArgs a) {
     const int64_t bs = row / a.H;
     const int s = (int)(bs % a.S_q);
     const int b = (int)(bs / a.S_q);
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (a.o_acc != nullptr) {
-      if (a.o == nullptr) continue;
-      if (a.lse_acc[((int64_t)b * a.H + h) * a.S_q + s] != -INFINITY) {
-        const f32x4* src = (const f32x4*)(a.o_acc + row * a.D + 8 * c);
-        const f32x4 x0 = src[0], x1 = src[1];
-        out = (u32x4){pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]), pack_bf16(x1[0], x1[1]),
-                      pack_bf16(x1[2], x1[3])};
-      }
-    } else if (a.lse != nullptr && c == 0) {
-      a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
-    }
-    *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = out;
+    write_empty(a, b, s, h, c);
   }
 }
 

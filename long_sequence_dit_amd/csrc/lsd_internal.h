@@ -18,6 +18,9 @@ struct AttnArgs {
   // blocks, read and replaced by its merge with this block's result.
   float* o_acc;       // [B, S_q, H, D] fp32 contiguous
   float* lse_acc;     // [B, H, S_q] fp32 contiguous
+  // Key-only padding mask: batch entry b attends its first kv_lens[b] keys
+  // (device array of B values, clamped to [0, S_kv]); null = all S_kv keys.
+  const int32_t* kv_lens;
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;

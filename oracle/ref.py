@@ -82,12 +82,24 @@ def _attend_block(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float):
     return o, lse
 
 
-def attention(q, k, v, scale=None):
-    """Dense, unmasked, bidirectional multi-head attention with LSE.
+def valid_keys(kv_lens, b: int, S_kv: int) -> int:
+    """Number of keys batch entry b attends: all S_kv, or kv_lens[b] clamped
+    to [0, S_kv] (the key-only padding mask)."""
+    if kv_lens is None:
+        return S_kv
+    return int(min(max(int(kv_lens[b]), 0), S_kv))
+
+
+def attention(q, k, v, scale=None, kv_lens=None):
+    """Dense, bidirectional multi-head attention with LSE.
 
     q: [B, S_q, H, D]; k, v: [B, S_kv, H, D] (bf16 bits or floats, any
     strides).  Returns O float64 [B, S_q, H, D] and LSE float64 [B, H, S_q].
-    [NVL72, The Scaling Challenge; Attention2D > Local Attention]
+    With ``kv_lens`` (B integers) batch entry b attends only its first
+    kv_lens[b] keys: the rest are padding with weight 0, and every query row,
+    padded or not, sees all valid keys.
+    [NVL72, The Scaling Challenge; Attention2D > Local Attention;
+    LTX-2 SP, Data flow (key-only padding mask)]
     """
     B, S_q, H, D = q.shape
     S_kv = k.shape[1]
@@ -96,9 +108,10 @@ def attention(q, k, v, scale=None):
     O = np.zeros((B, S_q, H, v.shape[3]))
     L = np.full((B, H, S_q), -np.inf)
     for b in range(B):
+        n = valid_keys(kv_lens, b, S_kv)
         for h in range(H):
-            kh = _as_f64(k[b, :, h, :])
-            vh = _as_f64(v[b, :, h, :])
+            kh = _as_f64(k[b, :n, h, :])
+            vh = _as_f64(v[b, :n, h, :])
             for r0 in range(0, S_q, _ROW_CHUNK):
                 qh = _as_f64(q[b, r0:r0 + _ROW_CHUNK, h, :])
                 o, lse = _attend_block(qh, kh, vh, sc)
@@ -107,14 +120,15 @@ def attention(q, k, v, scale=None):
     return O, L
 
 
-def attention_rows(q, k, v, b: int, h: int, rows: Iterable[int], scale=None):
+def attention_rows(q, k, v, b: int, h: int, rows: Iterable[int], scale=None, kv_lens=None):
     """Attention for selected query rows of one (batch, head), exact against
-    the full key set.  Returns (O [n, D], LSE [n]) float64."""
+    the full (valid) key set.  Returns (O [n, D], LSE [n]) float64."""
     rows = np.asarray(list(rows), dtype=np.int64)
     D = q.shape[3]
     sc = _default_scale(D, scale)
-    kh = _as_f64(k[b, :, h, :])
-    vh = _as_f64(v[b, :, h, :])
+    nk = valid_keys(kv_lens, b, k.shape[1])
+    kh = _as_f64(k[b, :nk, h, :])
+    vh = _as_f64(v[b, :nk, h, :])
     qh = _as_f64(q[b, rows, h, :])
     return _attend_block(qh, kh, vh, sc)
 
@@ -155,7 +169,7 @@ def merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     return O, lse
 
 
-def attention_accumulate(o_acc, lse_acc, q, k, v, scale=None):
+def attention_accumulate(o_acc, lse_acc, q, k, v, scale=None, kv_lens=None):
     """One Ring step with the merge folded in: the attention result of q
     against this key/value block, merged into the running result (O_acc,
     LSE_acc) of earlier blocks.  Where LSE_acc = -inf there is no history and
@@ -167,7 +181,7 @@ def attention_accumulate(o_acc, lse_acc, q, k, v, scale=None):
     running result with the online-softmax recurrence); Limitations and
     Future Work (the combine folded into the attention kernel)]
     """
-    O_b, L_b = attention(q, k, v, scale)
+    O_b, L_b = attention(q, k, v, scale, kv_lens)
     L_a = np.asarray(lse_acc, dtype=np.float64)
     none = np.transpose(np.isneginf(L_a), (0, 2, 1))[..., None]         # [B,S,H,1]
     O_a = np.where(none, 0.0, np.asarray(o_acc, dtype=np.float64))
@@ -175,11 +189,11 @@ def attention_accumulate(o_acc, lse_acc, q, k, v, scale=None):
 
 
 def attention_accumulate_rows(o_acc_rows, lse_acc_rows, q, k, v, b: int, h: int, rows: Iterable[int],
-                              scale=None):
+                              scale=None, kv_lens=None):
     """``attention_accumulate`` for selected query rows of one (batch, head):
     o_acc_rows [n, D] and lse_acc_rows [n] are the running result of those
     rows.  Returns (O [n, D], LSE [n]) float64."""
-    O_b, L_b = attention_rows(q, k, v, b, h, rows, scale)
+    O_b, L_b = attention_rows(q, k, v, b, h, rows, scale, kv_lens)
     L_a = np.asarray(lse_acc_rows, dtype=np.float64)
     O_a = np.where(np.isneginf(L_a)[:, None], 0.0, np.asarray(o_acc_rows, dtype=np.float64))
     n, D = O_b.shape

@@ -187,6 +187,52 @@ def pin_scale_argument():
     assert np.allclose(O2, O3, rtol=0, atol=1e-12) and np.allclose(L2, L3, rtol=0, atol=1e-12)
 
 
+def pin_key_mask():
+    """The key-only padding mask: batch entry b attends its first kv_lens[b]
+    keys.  Pads filled with huge values change nothing; the result equals the
+    unmasked oracle on the truncated keys, a pure-Python brute force of the
+    masked definition on a tiny case, and 0 / -inf for no valid keys; lengths
+    are clamped to [0, S_kv]; every query row (padded ones included) gets a
+    distribution over the valid keys."""
+    B, Sq, Skv, H, D = 3, 11, 23, 2, 64
+    q = _rand((B, Sq, H, D), 41)
+    k = _rand((B, Skv, H, D), 42).copy()
+    v = _rand((B, Skv, H, D), 43).copy()
+    lens = [23, 9, 0]
+    O, L = ref.attention(q, k, v, kv_lens=lens)
+    k[1, 9:] = _bits_of(3.0e4)
+    v[1, 9:] = _bits_of(-7.0e3)
+    k[2] = _bits_of(1.0e3)
+    O2, L2 = ref.attention(q, k, v, kv_lens=lens)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2), "padding keys leaked into the result"
+    for b, n in enumerate(lens):
+        Ot, Lt = ref.attention(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n])
+        assert np.allclose(O[b], Ot[0], rtol=0, atol=1e-13) and np.allclose(L[b], Lt[0], rtol=0, atol=1e-13)
+    assert np.all(O[2] == 0) and np.all(np.isneginf(L[2]))
+    Oc, Lc = ref.attention(q, k, v, kv_lens=[99, -5, 0])
+    O0, L0 = ref.attention(q, k, v, kv_lens=[23, 0, 0])
+    assert np.array_equal(Oc, O0) and np.array_equal(Lc, L0), "kv_lens not clamped to [0, S_kv]"
+    # brute force, tiny: explicit loops over the valid keys only
+    qt = _rand((1, 3, 1, 4), 44)
+    kt = _rand((1, 5, 1, 4), 45)
+    vt = _rand((1, 5, 1, 4), 46)
+    Ob, Lb = ref.attention(qt, kt, vt, scale=0.5, kv_lens=[3])
+    qf, kf, vf = (_dec(x).tolist() for x in (qt, kt, vt))
+    for i in range(3):
+        logits = [0.5 * sum(qf[0][i][0][d] * kf[0][j][0][d] for d in range(4)) for j in range(3)]
+        m = max(logits)
+        ws = [math.exp(x - m) for x in logits]
+        tot = sum(ws)
+        assert abs(Lb[0, 0, i] - (m + math.log(tot))) < 1e-12
+        for d in range(4):
+            want = sum(ws[j] * vf[0][j][0][d] for j in range(3)) / tot
+            assert abs(Ob[0, i, 0, d] - want) < 1e-12
+    # rows_variant agrees and puts no weight on padding
+    rows = [0, 5, 10]
+    o_r, l_r = ref.attention_rows(q, k, v, 1, 1, rows, kv_lens=lens)
+    assert np.allclose(o_r, O[1, rows, 1], rtol=0, atol=1e-13) and np.allclose(l_r, L[1, 1, rows], rtol=0, atol=1e-13)
+
+
 # ----------------------------------------------------------------- merge
 
 def _partials(q, k, v, bounds):
@@ -409,7 +455,7 @@ def pin_relayout_head_limit():
 
 ATTENTION_PINS = [pin_identical_keys, pin_dominant_logit, pin_rows_sum_to_one, pin_single_key,
                   pin_no_keys, pin_library_softmax, pin_brute_force_tiny,
-                  pin_permutation_and_scaling, pin_scale_argument]
+                  pin_permutation_and_scaling, pin_scale_argument, pin_key_mask]
 MERGE_PINS = [pin_merge_equals_full, pin_merge_attention2d_grid, pin_merge_closed_forms,
               pin_ring_streaming_merge]
 ACCUMULATE_PINS = [pin_accumulate_streams_to_full, pin_accumulate_special_cases]

@@ -209,6 +209,35 @@ def test_relayout_head_to_seq_validation():
     assert r == LSD_EINVAL and "overlaps" in msg
 
 
+def test_attn_fwd_masked_and_accumulate_validation():
+    L = lsd.lib()
+    q, k, v, o = good4()
+    lens = BASE + 9 * GB
+    r = L.lsd_attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, ctypes.byref(o), None,
+                              ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "kv_lens" in L.lsd_last_error().decode()
+    r = L.lsd_attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.c_void_p(lens + 2),
+                              ctypes.byref(o), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "aligned" in L.lsd_last_error().decode()
+    # an output overlapping kv_lens
+    r = L.lsd_attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.c_void_p(BASE + 3 * GB),
+                              ctypes.byref(o), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "overlaps" in L.lsd_last_error().decode()
+    acc, lacc = BASE + 10 * GB, BASE + 11 * GB
+    r = L.lsd_attn_fwd_accumulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, None,
+                                  ctypes.c_void_p(lacc), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "o_acc" in L.lsd_last_error().decode()
+    r = L.lsd_attn_fwd_accumulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.c_void_p(acc + 4), ctypes.c_void_p(lacc), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "16-byte" in L.lsd_last_error().decode()
+    r = L.lsd_attn_fwd_accumulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.c_void_p(acc), ctypes.c_void_p(acc + 64), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "overlaps" in L.lsd_last_error().decode()
+    r = L.lsd_attn_fwd_accumulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.c_void_p(BASE + 64), ctypes.c_void_p(lacc), None, ctypes.c_float(0.0), None)
+    assert r == LSD_EINVAL and "overlaps" in L.lsd_last_error().decode()
+
+
 def test_attn_fwd_rejects_huge_kv_stride():
     q, k, v, o = good4()
     k = view(BASE + GB, (1, 256, 2, 64), [256 * (1 << 24), 1 << 24, 64, 1])

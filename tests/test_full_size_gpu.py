@@ -52,6 +52,20 @@ def test_ltx2_scale():
     check_rows(o, lse, q, k, v, range(32), 1, "LTX-2")
 
 
+def test_ltx2_scale_key_padding_mask():
+    note("full LTX-2 with a key-only mask: 21,000 of 24,576 keys valid, NaN padding")
+    t = torch()
+    q, k, v = synth.ltx2_qkv()
+    n = 21_000
+    k = k.copy()
+    v = v.copy()
+    k[:, n:] = 0x7FC1
+    v[:, n:] = 0x7FC1
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v), kv_lens=t.tensor([n], dtype=t.int32, device="cuda"))
+    t.cuda.synchronize()
+    check_rows(o, lse, q, k[:, :n], v[:, :n], range(0, 32, 5), 11, "LTX-2 masked")
+
+
 def test_wan_ulysses_share_relayout_then_attention():
     note("full Wan Ulysses share: fused QKV [2,75600,3,40,128] -> rank slices, P=4")
     t = torch()

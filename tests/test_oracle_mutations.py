@@ -217,3 +217,27 @@ INVERSE_MUTANTS = [_inverse_next_shard, _inverse_reversed_ranks]
 def test_inverse_relayout_mutant_is_caught(monkeypatch, mutant):
     monkeypatch.setattr(ref, "relayout_head_to_seq", mutant)
     assert _run(pins.RELAYOUT_PINS), f"{mutant.__name__} passed every relayout pin"
+
+
+_orig_valid_keys = ref.valid_keys
+
+
+def _mask_ignored(kv_lens, b, S_kv):
+    return S_kv
+
+
+def _mask_one_extra(kv_lens, b, S_kv):
+    return min(_orig_valid_keys(kv_lens, b, S_kv) + 1, S_kv)
+
+
+def _mask_unclamped(kv_lens, b, S_kv):
+    return S_kv if kv_lens is None else int(kv_lens[b])
+
+
+MASK_MUTANTS = [_mask_ignored, _mask_one_extra, _mask_unclamped]
+
+
+@pytest.mark.parametrize("mutant", MASK_MUTANTS, ids=lambda f: f.__name__)
+def test_key_mask_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "valid_keys", mutant)
+    assert _run(pins.ATTENTION_PINS), f"{mutant.__name__} passed every attention pin"
