@@ -1,0 +1,117 @@
+"""Float64 CPU oracle for the FP8 attention inputs: the E4M3 code, the cast of
+Q, K, V to FP8 with one scale per (tensor, batch, head), and attention over
+the FP8 inputs.
+
+Test infrastructure only, like the rest of this package.
+
+Source: [NVL72] "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+"Ulysses Parallelism > Fused vs. unfused QKV all-to-all": the stacked QKV
+buffer gets one FP8 cast pass before the attention kernel, in a layout the
+kernel reads directly.
+
+Readings where the pages are silent (also in the design notes):
+* Format: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+  largest finite 448; codes 0x7F / 0xFF are NaN; no infinities).
+* Scale: one per (tensor, batch, head), from the absolute maximum over that
+  head's tokens and channels: the value x is coded as E4M3(x * (448 / amax))
+  with the product rounded to float32 and the code rounded to nearest, ties
+  to even; a head that is all zero uses the factor 1 (its codes are 0).
+  Dequantised value: decode(code) * (amax / 448) in float32 arithmetic.
+* FP8 attention computes the attention of the dequantised inputs: its
+  definition is ``attention`` applied to them.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import ref
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Exact value of each E4M3 code (NaN for 0x7F / 0xFF), float64."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.exp2(e.astype(np.float64) - 10.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+# every finite magnitude code 0x00..0x7E with its value, ascending
+_MAG_CODES = np.arange(0x7F, dtype=np.int64)
+_MAG_VALUES = e4m3_decode(_MAG_CODES)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest E4M3 code, ties to the even code
+    (even mantissa); magnitudes above 464 (past the midpoint between 448 and
+    the next step, 480) become NaN (0x7F with the sign), as there is no
+    infinity.  The sign of zero is kept."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    # index of the largest code value <= mag
+    lo = np.clip(np.searchsorted(_MAG_VALUES, mag, side="right") - 1, 0, 0x7E)
+    hi = np.clip(lo + 1, 0, 0x7E)
+    d_lo = mag - _MAG_VALUES[lo]
+    d_hi = _MAG_VALUES[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi != lo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo)
+    # beyond 448 the next step would be 480: 464 is the midpoint, which rounds
+    # to the even mantissa (448); anything larger overflows to NaN
+    code = np.where(mag > 464.0, 0x7F, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def head_amax(x) -> np.ndarray:
+    """max |x| over tokens and channels for every (batch, head): [B, H]."""
+    v = np.abs(ref._as_f64(x))
+    return v.max(axis=(1, 3)) if v.shape[1] > 0 else np.zeros((v.shape[0], v.shape[2]))
+
+
+def quantize(x, amax: np.ndarray) -> np.ndarray:
+    """E4M3 codes of x [B, S, H, D] with the per-(batch, head) factor
+    448 / amax, computed in float32 as the scale rule states."""
+    a32 = np.asarray(amax, dtype=np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(a32 > 0, np.float32(E4M3_MAX) / np.where(a32 > 0, a32, np.float32(1)), np.float32(1))
+    inv = inv.astype(np.float32)
+    xf = ref._as_f64(x).astype(np.float32)                         # bf16 values are exact in float32
+    prod = (xf * inv[:, None, :, None]).astype(np.float32)         # one float32 rounding
+    return e4m3_encode(prod)
+
+
+def cast_qkv(q, k, v):
+    """The single FP8 cast pass over Q, K, V: codes for each tensor and the
+    amax array [3, B, H] (q, k, v)."""
+    amax = np.stack([head_amax(q), head_amax(k), head_amax(v)]).astype(np.float32)
+    return quantize(q, amax[0]), quantize(k, amax[1]), quantize(v, amax[2]), amax
+
+
+def dequantize(codes, amax) -> np.ndarray:
+    """decode(code) * (amax / 448), the scale applied in float32."""
+    s = (np.asarray(amax, dtype=np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_decode(codes) * s.astype(np.float64)[:, None, :, None]
+
+
+def attention_fp8(q8, k8, v8, q_amax, k_amax, v_amax, scale=None):
+    """Attention over the dequantised FP8 inputs (codes [B, S, H, D] and
+    per-(batch, head) amax): (O, LSE) float64."""
+    return ref.attention(dequantize(q8, q_amax), dequantize(k8, k_amax), dequantize(v8, v_amax), scale)
+
+
+def attention_fp8_rows(q8, k8, v8, q_amax, k_amax, v_amax, b: int, h: int, rows, scale=None):
+    """``attention_fp8`` for selected query rows of one (batch, head)."""
+    sq = np.float32(np.float32(q_amax[b, h]) / np.float32(E4M3_MAX))
+    sk = np.float32(np.float32(k_amax[b, h]) / np.float32(E4M3_MAX))
+    sv = np.float32(np.float32(v_amax[b, h]) / np.float32(E4M3_MAX))
+    rows = np.asarray(list(rows), dtype=np.int64)
+    qh = e4m3_decode(q8[b, rows, h, :]) * float(sq)
+    kh = e4m3_decode(k8[b, :, h, :]) * float(sk)
+    vh = e4m3_decode(v8[b, :, h, :]) * float(sv)
+    return ref._attend_block(qh, kh, vh, ref._default_scale(q8.shape[3], scale))

@@ -462,3 +462,111 @@ ACCUMULATE_PINS = [pin_accumulate_streams_to_full, pin_accumulate_special_cases]
 RELAYOUT_PINS = [pin_relayout_index_map, pin_relayout_identity_and_round_trip, pin_relayout_head_limit,
                  pin_relayout_inverse_index_map]
 ALL_PINS = ATTENTION_PINS + MERGE_PINS + ACCUMULATE_PINS + RELAYOUT_PINS
+
+
+# ----------------------------------------------------------------- fp8
+
+def pin_e4m3_code_table():
+    """OCP E4M3 facts: 0x7E = 448 (largest), 0x08 = 2^-6 (smallest normal),
+    0x01 = 2^-9 (smallest subnormal), 0x38 = 1, 0xB8 = -1, 0x7F / 0xFF NaN;
+    every finite code decodes and re-encodes to itself; values are monotonic
+    in the code."""
+    from oracle import fp8
+    d = fp8.e4m3_decode
+    assert d(0x7E) == 448.0 and d(0x08) == 2.0 ** -6 and d(0x01) == 2.0 ** -9
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0 and d(0x40) == 2.0 and d(0x3C) == 1.5
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF)) and d(0x00) == 0.0
+    codes = np.arange(256)
+    fin = (codes & 0x7F) != 0x7F
+    vals = d(codes)
+    assert np.array_equal(fp8.e4m3_encode(vals[fin]), codes[fin].astype(np.uint8))
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def pin_e4m3_rounding():
+    """Round to nearest, ties to even: midpoints between neighbouring codes
+    go to the even mantissa, points just off a midpoint go to the nearer code;
+    464 (the midpoint above 448) rounds to 448 and larger values overflow to
+    NaN; the sign of zero is kept."""
+    from oracle import fp8
+    vals = fp8.e4m3_decode(np.arange(0x7F))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    got = fp8.e4m3_encode(mids)
+    for i, c in enumerate(got):
+        even = i if i % 2 == 0 else i + 1
+        assert c == even, f"midpoint {mids[i]} -> {c:#x}, want {even:#x}"
+    eps = 1e-9
+    assert np.array_equal(fp8.e4m3_encode(mids - eps * mids), np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(fp8.e4m3_encode(mids + eps * mids), np.arange(1, 0x7F, dtype=np.uint8))
+    assert fp8.e4m3_encode(np.array([464.0]))[0] == 0x7E
+    assert fp8.e4m3_encode(np.array([464.01]))[0] == 0x7F
+    assert fp8.e4m3_encode(np.array([-1e9]))[0] == 0xFF
+    assert fp8.e4m3_encode(np.array([-0.0]))[0] == 0x80 and fp8.e4m3_encode(np.array([0.0]))[0] == 0x00
+    # relative error of normal values is at most half an ulp (2^-4)
+    x = np.linspace(2.0 ** -6, 448.0, 10001)
+    err = np.abs(fp8.e4m3_decode(fp8.e4m3_encode(x)) - x) / x
+    assert err.max() <= 2.0 ** -4 + 1e-15
+
+
+def pin_fp8_cast():
+    """The cast: the largest magnitude of each (tensor, batch, head) codes to
+    +-448 exactly; an all-zero head codes to zeros; values already on the
+    FP8 grid of their head's scale are reproduced exactly; every dequantised
+    value is within half an FP8 ulp (plus the subnormal step) of the input."""
+    from oracle import fp8
+    B, S, H, D = 2, 37, 3, 64
+    q = _rand((B, S, H, D), 51)
+    k = _rand((B, S, H, D), 52).copy()
+    v = _rand((B, S, H, D), 53)
+    k[1, :, 2, :] = 0                                           # an all-zero head
+    q8, k8, v8, amax = fp8.cast_qkv(q, k, v)
+    assert amax.shape == (3, B, H)
+    for x, c, a in ((q, q8, amax[0]), (k, k8, amax[1]), (v, v8, amax[2])):
+        xv = _dec(x)
+        for b in range(B):
+            for h in range(H):
+                if a[b, h] == 0:
+                    assert np.all(c[b, :, h] & 0x7F == 0)
+                    continue
+                i = np.unravel_index(np.argmax(np.abs(xv[b, :, h])), xv[b, :, h].shape)
+                assert (c[b, :, h][i] & 0x7F) == 0x7E
+        deq = fp8.dequantize(c, a)
+        step = (np.asarray(a, np.float64) / 448.0)[:, None, :, None]
+        assert np.all(np.abs(deq - xv) <= np.abs(xv) * 2.0 ** -4 + step * 2.0 ** -9 * 1.01)
+    # exactly representable inputs: codes times a power-of-two scale
+    codes = np.random.Generator(np.random.PCG64(54)).integers(0, 0x7F, size=(1, 16, 1, 32)).astype(np.uint8)
+    codes[0, 3, 0, 5] = 0x7E                                    # amax = 448 -> factor 1
+    xb = synth.f32_to_bf16_bits(fp8.e4m3_decode(codes).astype(np.float32))
+    assert np.array_equal(fp8.quantize(xb, fp8.head_amax(xb)), codes)
+
+
+def pin_fp8_attention():
+    """FP8 attention is attention of the dequantised inputs: with inputs that
+    the cast reproduces exactly it equals attention of the originals, and a
+    uniform positive rescaling of one tensor's codes' scale (amax) scales the
+    dequantised values and so the logits or outputs accordingly."""
+    from oracle import fp8
+    g = np.random.Generator(np.random.PCG64(55))
+    def on_grid(shape):
+        c = g.integers(0, 0x7F, size=shape).astype(np.uint8) | (g.integers(0, 2, size=shape).astype(np.uint8) << 7)
+        c[..., 0, :, 0] = 0x7E                                  # amax 448 per (b, h)
+        return c
+    B, S, H, D = 1, 40, 2, 64
+    q8, k8, v8 = on_grid((B, S, H, D)), on_grid((B, S, H, D)), on_grid((B, S, H, D))
+    amax = np.full((B, H), 448.0, np.float32)
+    O, L = fp8.attention_fp8(q8, k8, v8, amax, amax, amax, scale=1e-4)
+    O2, L2 = ref.attention(fp8.e4m3_decode(q8), fp8.e4m3_decode(k8), fp8.e4m3_decode(v8), scale=1e-4)
+    assert np.allclose(O, O2, rtol=0, atol=1e-12) and np.allclose(L, L2, rtol=0, atol=1e-12)
+    # v scale 2x -> O 2x; q scale 2x with scale/2 -> same result
+    O3, L3 = fp8.attention_fp8(q8, k8, v8, amax, amax, 2 * amax, scale=1e-4)
+    assert np.allclose(O3, 2 * O, rtol=0, atol=1e-9) and np.allclose(L3, L, rtol=0, atol=1e-12)
+    O4, L4 = fp8.attention_fp8(q8, k8, v8, 2 * amax, amax, amax, scale=0.5e-4)
+    assert np.allclose(O4, O, rtol=0, atol=1e-12) and np.allclose(L4, L, rtol=0, atol=1e-12)
+    rows = [0, 17, 39]
+    o_r, l_r = fp8.attention_fp8_rows(q8, k8, v8, amax, amax, amax, 0, 1, rows, scale=1e-4)
+    assert np.allclose(o_r, O[0, rows, 1], rtol=0, atol=1e-12) and np.allclose(l_r, L[0, 1, rows], rtol=0, atol=1e-12)
+
+
+FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_attention]
+ALL_PINS = ALL_PINS + FP8_PINS

@@ -241,3 +241,56 @@ MASK_MUTANTS = [_mask_ignored, _mask_one_extra, _mask_unclamped]
 def test_key_mask_mutant_is_caught(monkeypatch, mutant):
     monkeypatch.setattr(ref, "valid_keys", mutant)
     assert _run(pins.ATTENTION_PINS), f"{mutant.__name__} passed every attention pin"
+
+
+from oracle import fp8 as _fp8
+
+_orig_encode = _fp8.e4m3_encode
+_orig_decode = _fp8.e4m3_decode
+
+
+def _encode_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    c = _orig_encode(x)
+    vals = _orig_decode(np.arange(0x7F))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    hit = np.isin(np.abs(x), mids)
+    up = (np.searchsorted(vals, np.abs(x)) & 0x7F).astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)
+    return np.where(hit, up, c).astype(np.uint8)
+
+
+def _encode_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = _orig_decode(np.arange(0x7F))
+    lo = np.clip(np.searchsorted(vals, np.abs(x), side="right") - 1, 0, 0x7E)
+    return (lo | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _decode_fnuz_bias(c):
+    return _orig_decode(c) * 0.5
+
+
+_orig_head_amax = _fp8.head_amax
+
+
+def _amax_per_tensor(x):
+    a = _orig_head_amax(x)
+    return np.full_like(a, a.max())
+
+
+_orig_dequant = _fp8.dequantize
+
+
+def _dequant_no_scale(codes, amax):
+    return _orig_decode(codes)
+
+
+FP8_MUTANTS = [("e4m3_encode", _encode_ties_away), ("e4m3_encode", _encode_truncate),
+               ("e4m3_decode", _decode_fnuz_bias), ("head_amax", _amax_per_tensor),
+               ("dequantize", _dequant_no_scale)]
+
+
+@pytest.mark.parametrize("name,mutant", FP8_MUTANTS, ids=lambda f: getattr(f, "__name__", str(f)))
+def test_fp8_mutant_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(_fp8, name, mutant)
+    assert _run(pins.FP8_PINS), f"{mutant.__name__} passed every fp8 pin"
