@@ -38,12 +38,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attention TFLOP/s + % bf16 MFMA peak (1 GPU); merge/relayout GB/s % HBM"
 
 WORKLOADS = {
     "ltx2": dict(desc="LTX-2 scale: fused QKV [1,24576,3,32,128] -> relayout (P=1) -> attention over 2 K/V "
                       "blocks with fp32 LSE -> LSE merge", B=1, S=24_576, H=32, D=128, P=1, kv_blocks=2, seed=1),
+    "ltx2_fp8": dict(desc="LTX-2 scale on the FP8 path: fused QKV [1,24576,3,32,128] -> relayout (P=1) -> one "
+                          "FP8 cast of Q,K,V (per-head scales) -> FP8 attention over all 24576 keys with fp32 LSE",
+                     B=1, S=24_576, H=32, D=128, P=1, kv_blocks=1, seed=1, fp8=True),
     "wan": dict(desc="Wan 2.2 A14B Ulysses share: fused QKV [2,75600,3,40,128] -> relayout P=4 rank 0 "
                      "-> attention [2,75600,10,128] with fp32 LSE -> inverse relayout of O (this rank's slice "
                      "and 3 stand-in slices of the other ranks) -> shard [2,18900,40,128]", B=2, S=75_600, H=40,
@@ -93,8 +97,8 @@ class Pipeline:
         self.lsd, self.torch, self.name, self.w = lsd, torch, name, w
         B, S, H, D = w["B"], w["S"], w["H"], w["D"]
         self.host = {}
-        if name in ("ltx2", "tiny", "wan"):
-            if name == "ltx2":
+        if name in ("ltx2", "ltx2_fp8", "tiny", "wan"):
+            if name in ("ltx2", "ltx2_fp8"):
                 q, k, v = synth.ltx2_qkv(seed=w["seed"], S=S, H=H, D=D)
                 fused = np.stack([q, k, v], axis=2)          # [B,S,3,H,D], the projection's layout
                 del q, k, v
@@ -139,7 +143,12 @@ class Pipeline:
         if nb > 1:
             self.o = torch.empty((B, self.S_q, Hq, D), dtype=torch.bfloat16, device="cuda")
             self.lse = torch.empty((B, Hq, self.S_q), dtype=torch.float32, device="cuda")
-        self.has_relayout = name in ("ltx2", "tiny", "wan")
+        self.has_relayout = name in ("ltx2", "ltx2_fp8", "tiny", "wan")
+        self.fp8 = bool(w.get("fp8"))
+        if self.fp8:
+            self.fp8_bufs = lsd.fp8_buffers(B, self.qkv[0].shape[1], self.qkv[0].shape[2], D)
+            # two passes over the bf16 inputs (amax, then codes) and one byte per element out
+            self.cast_bytes = 3 * B * self.qkv[0].shape[1] * self.qkv[0].shape[2] * D * (2 + 2 + 1)
         self.stream = bool(w.get("stream"))
         self.has_merge = nb > 1 and not self.stream
         if self.stream:
@@ -192,6 +201,14 @@ class Pipeline:
             lsd.relayout_seq_to_head(self.src, self.w["P"], 0, dst=self.qkv)
             mark()
         q, kk, v = self.qkv
+        if self.fp8:
+            mark()
+            q8, k8, v8, amax = lsd.cast_qkv_fp8(q, kk, v, out=self.fp8_bufs)
+            mark()
+            mark()
+            lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2], o=self.o_parts[0], lse=self.lse_parts[0])
+            mark()
+            return k
         if self.stream:
             self.lse_acc.fill_(float("-inf"))          # no history yet
         for i, (lo, hi) in enumerate(self.bounds):
@@ -216,6 +233,8 @@ class Pipeline:
 
     def kernel_names(self):
         names = ["relayout"] if self.has_relayout else []
+        if self.fp8:
+            return names + ["cast_fp8", "attn_fwd"]
         names += ["attn_fwd"] * len(self.bounds)
         if self.has_merge:
             names.append("attn_merge")
@@ -274,18 +293,31 @@ def cpu_baseline(pipe, budget_s):
     else:
         t_rel = 0.0
         q, k, v = h["q"], h["k"], h["v"]
+    # FP8 path: the oracle's cast of two heads (scaled to all heads), whose codes
+    # then feed the attention sample
+    t_cast = 0.0
+    heads = [(b, hh) for b in range(B) for hh in range(Hq)]
+    if pipe.fp8:
+        from oracle import fp8 as ofp8
+        nh = min(2, Hq)
+        t0 = time.perf_counter()
+        c8 = ofp8.cast_qkv(q[:1, :, :nh], k[:1, :, :nh], v[:1, :, :nh])
+        t_cast = (time.perf_counter() - t0) * (B * Hq) / nh
+        heads = [(0, hh) for hh in range(nh)]
     # attention: chunks of 256 query rows, cycling over (b, h), until the budget
     rows_done = 0
     t_attn = 0.0
     g = np.random.Generator(np.random.PCG64(123))
-    heads = [(b, hh) for b in range(B) for hh in range(Hq)]
     i = 0
     while t_attn < budget_s and i < 64 * len(heads):
         b, hh = heads[i % len(heads)]
         r0 = int(g.integers(0, max(1, pipe.S_q - 256)))
         rows = np.arange(r0, min(pipe.S_q, r0 + 256))
         t0 = time.perf_counter()
-        ref.attention_rows(q, k, v, b, hh, rows, kv_lens=pipe.kv_lens)
+        if pipe.fp8:
+            ofp8.attention_fp8_rows(c8[0], c8[1], c8[2], c8[3][0], c8[3][1], c8[3][2], b, hh, rows)
+        else:
+            ref.attention_rows(q, k, v, b, hh, rows, kv_lens=pipe.kv_lens)
         t_attn += time.perf_counter() - t0
         rows_done += rows.size
         i += 1
@@ -310,7 +342,7 @@ def cpu_baseline(pipe, budget_s):
         ref.relayout_head_to_seq(slices, P, 0)
         t_inv = time.perf_counter() - t0
         del slices
-    t_step = t_rel + t_attn_full + t_merge_full + t_inv
+    t_step = t_rel + t_cast + t_attn_full + t_merge_full + t_inv
     return {
         "value": pipe.flops / t_step / 1e12,
         "unit": "TFLOP/s",
@@ -321,6 +353,8 @@ def cpu_baseline(pipe, budget_s):
                    + (f"; relayout timed in full ({t_rel:.2f} s)" if t_rel else "")
                    + (f"; merge timed on a {min(pipe.S_q, 512)}-position slab, scaled" if pipe.has_merge else "")
                    + (f"; inverse relayout timed in full ({t_inv:.2f} s)" if pipe.has_inverse else "")
+                   + (f"; FP8 cast timed on 2 heads, scaled ({t_cast:.2f} s); attention rows on their codes"
+                      if pipe.fp8 else "")
                    + f"; extrapolated step {t_step:.1f} s; host has {cores} cores, BLAS threads {blas_threads}"),
     }
 
@@ -377,10 +411,16 @@ def main():
             if n == "attn_fwd":
                 attn_flops.append(pipe.attn_flops_per_launch[ai])
                 ai += 1
+    peak = PEAK_FP8_TFLOPS if pipe.fp8 else PEAK_BF16_TFLOPS
     attn_ms = float(np.mean(dur["attn_fwd"]))
     attn_tflops = float(np.sum(attn_flops) / (np.sum(dur["attn_fwd"]) * 1e-3)) / 1e12
     kernels = {"attn_fwd": {"launches_per_step": len(pipe.bounds), "avg_ms": round(attn_ms, 4),
-                            "TFLOP/s": round(attn_tflops, 1), "frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}}
+                            "TFLOP/s": round(attn_tflops, 1), "frac_mfma_peak": round(attn_tflops / peak, 4)}}
+    if pipe.fp8:
+        ms = float(np.mean(dur["cast_fp8"]))
+        gbs = pipe.cast_bytes / (ms * 1e-3) / 1e9
+        kernels["cast_fp8"] = {"avg_ms": round(ms, 4), "bytes": pipe.cast_bytes, "GB/s": round(gbs, 1),
+                               "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "launches": 3}
     if pipe.has_relayout:
         ms = float(np.mean(dur["relayout"]))
         gbs = pipe.relayout_bytes / (ms * 1e-3) / 1e9
@@ -410,14 +450,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if pipe.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w["desc"], "B": w["B"], "S_q": pipe.S_q, "S_kv": pipe.S_kv, "H": pipe.Hq,
                    "D": w["D"], "kv_blocks": w["kv_blocks"], "fused_merge": pipe.stream,
                    "flop_per_step": pipe.flops},
         "roofline": {"bound": "mfma", "achieved": round(flops_per_launch / (attn_ms * 1e-3) / 1e12, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops_per_launch / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops_per_launch / (attn_ms * 1e-3) / 1e12 / peak, 4),
                      "traffic": traffic, "kernel": "attn_fwd",
                      "flop_per_launch": flops_per_launch, "avg_launch_ms": round(attn_ms, 4)},
         "kernels": kernels,

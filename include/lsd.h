@@ -10,6 +10,8 @@
  *   lsd_attn_fwd_accumulate   the same against one K/V block, merged in place
  *                             into a running (O, LSE) (Ring step)
  *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
+ *   lsd_cast_qkv_fp8          one FP8 cast of Q, K, V (per-head scales)
+ *   lsd_attn_fwd_fp8          attention on the FP8 inputs
  *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
  *                             after attention)
  *
@@ -171,6 +173,62 @@ lsd_status lsd_attn_fwd_accumulate(const lsd_view4* q, const lsd_view4* k, const
  */
 lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* lse_parts,
                           const lsd_view4* o_out, float* lse_out, void* stream);
+
+/*
+ * One FP8 cast pass over Q, K and V, producing the inputs of lsd_attn_fwd_fp8.
+ *
+ * Defined by "Scaling Video Generation Across NVL72 rack with TensorRT-LLM",
+ * "Ulysses Parallelism > Fused vs. unfused QKV all-to-all": the stacked QKV
+ * buffer gets a single FP8 cast pass before the attention kernel (not three
+ * casts), landing in a layout the kernel reads without another copy.
+ *
+ *   src   3 bf16 views (B, S, H, D): Q, K, V (e.g. strided views of a fused
+ *         [B, S, 3, H, D] buffer), one shape, D = 128
+ *   dst   3 FP8 E4M3 views (B, S, H, D), one byte per element, strides in
+ *         bytes: dst[0] (Q) and dst[1] (K) with channels contiguous
+ *         (stride[3] = 1); dst[2] (V) stored transposed, tokens contiguous
+ *         (stride[1] = 1), stride[3] = row pitch of one (b, h, d) row, at
+ *         least S rounded up to 64: the cast also writes zero codes for the
+ *         tokens S .. that bound (each row must be allocated that far)
+ *   amax  float32 [3, B, H]: max |x| over tokens and channels of each
+ *         (tensor, batch, head), written
+ *
+ * code = E4M3(x * (448 / amax)): the product rounded to float32, the code to
+ * nearest, ties to even (OCP E4M3: largest finite 448); a head whose amax is
+ * 0 uses factor 1.  The dequantised value is code * (amax / 448).  All other
+ * byte strides and pointers must be multiples of 16.  Deterministic (the amax
+ * reduction takes maxima, which do not depend on order).  Three launches on
+ * `stream`.
+ */
+lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream);
+
+/*
+ * Dense bidirectional attention over FP8 inputs: the attention of the
+ * dequantised values, computed on FP8 matrix cores.
+ *
+ * Defined as lsd_attn_fwd of q = code_q * s_q, k = code_k * s_k,
+ * v = code_v * s_v with s = amax / 448 per (b, h) ("Scaling Video Generation
+ * Across NVL72 rack with TensorRT-LLM", "Ulysses Parallelism > Fused vs.
+ * unfused QKV all-to-all" and "The Scaling Challenge in Video Generation").
+ *
+ *   q8, k8   E4M3 (B, S_q, H, D) and (B, S_kv, H, D) views, channels
+ *            contiguous, as lsd_cast_qkv_fp8 writes them
+ *   v8       E4M3 (B, S_kv, H, D) view stored transposed (tokens contiguous,
+ *            stride[3] = row pitch); every row must be readable, with finite
+ *            codes, up to S_kv rounded up to 64 tokens from the view's start
+ *            (the cast's padded rows satisfy this for views that start at a
+ *            multiple of 64 tokens), and stride[3] must be at least that
+ *   q_amax, k_amax, v_amax  float32 [B, H]: the amax of each tensor
+ *   o        bf16 (B, S_q, H, D), written;  lse  float32 [B, H, S_q] or NULL
+ *
+ * D = 128 only.  The softmax weights are rounded to E4M3 for the PV product
+ * (the row sums stay float32), so O carries an error of up to 2^-4 of
+ * sum_j p_j |v_j| / l (see the design notes for the full bound); LSE is as
+ * exact as in lsd_attn_fwd.  S_kv == 0 gives O = 0, LSE = -inf.
+ */
+lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
+                            const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
+                            float softmax_scale, void* stream);
 
 /*
  * Ulysses sequence-major -> head-major relayout for one destination rank.

@@ -59,6 +59,11 @@ def lib():
         L.lsd_attn_fwd_accumulate.restype = ctypes.c_int
         L.lsd_attn_fwd_accumulate.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, P(View4), ctypes.c_float, ctypes.c_void_p]
+        L.lsd_cast_qkv_fp8.restype = ctypes.c_int
+        L.lsd_cast_qkv_fp8.argtypes = [P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p]
+        L.lsd_attn_fwd_fp8.restype = ctypes.c_int
+        L.lsd_attn_fwd_fp8.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, P(View4), ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
         L.lsd_relayout_head_to_seq.restype = ctypes.c_int
         L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
@@ -194,6 +199,69 @@ def attn_merge(o_parts: Sequence, lse_parts: Sequence, o=None, lse=None, return_
     lp = _f32_ptr(lse, "lse", (B, H, S)) if lse is not None else None
     st = lib().lsd_attn_merge(n, views, ptrs, ctypes.byref(vo), lp, _stream(o))
     _check(st, "lsd_attn_merge")
+    return (o, lse) if lse is not None else o
+
+
+def _view8(t, name):
+    """View of a one-byte-per-element tensor (strides in bytes)."""
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must be in GPU memory")
+    if t.element_size() != 1 or t.dim() != 4:
+        raise ValueError(f"{name}: expected a 4-d tensor of one-byte elements (FP8 codes)")
+    v = View4()
+    v.data = t.data_ptr()
+    for i in range(4):
+        v.shape[i] = t.shape[i]
+        v.stride[i] = t.stride(i)
+    return v
+
+
+def fp8_buffers(B, S, H, D=128, device="cuda"):
+    """Allocate the outputs of ``cast_qkv_fp8``: q8, k8 (B, S, H, D) and v8, the
+    (B, S, H, D) view of V stored transposed with rows padded to a multiple of
+    64 tokens (storage [B, H, D, S_pad]), plus amax [3, B, H]."""
+    torch = _torch()
+    s_pad = (S + 63) // 64 * 64
+    q8 = torch.empty((B, S, H, D), dtype=torch.float8_e4m3fn, device=device)
+    k8 = torch.empty((B, S, H, D), dtype=torch.float8_e4m3fn, device=device)
+    vt = torch.empty((B, H, D, s_pad), dtype=torch.float8_e4m3fn, device=device)
+    v8 = vt.permute(0, 3, 1, 2)[:, :S]
+    amax = torch.empty((3, B, H), dtype=torch.float32, device=device)
+    return q8, k8, v8, amax
+
+
+def cast_qkv_fp8(q, k, v, out=None):
+    """One FP8 (E4M3) cast of Q, K, V (bf16 (B, S, H, D) views) with one scale
+    per (tensor, batch, head).  Returns (q8, k8, v8, amax): v8 is a (B, S, H, D)
+    view of V stored transposed; amax[t] is tensor t's per-(b, h) amax."""
+    B, S, H, D = q.shape
+    if out is None:
+        out = fp8_buffers(B, S, H, D, q.device)
+    q8, k8, v8, amax = out
+    sv = (View4 * 3)(_view(q, "q"), _view(k, "k"), _view(v, "v"))
+    dv = (View4 * 3)(_view8(q8, "q8"), _view8(k8, "k8"), _view8(v8, "v8"))
+    st = lib().lsd_cast_qkv_fp8(sv, dv, _f32_ptr(amax, "amax", (3, B, H)), _stream(q))
+    _check(st, "lsd_cast_qkv_fp8")
+    return q8, k8, v8, amax
+
+
+def attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o=None, lse=None, scale: Optional[float] = None,
+                 return_lse: bool = True):
+    """Attention over FP8 inputs (as ``cast_qkv_fp8`` produces them): the
+    attention of the dequantised values, O in bf16 and the LSE."""
+    torch = _torch()
+    B, S_q, H, D = q8.shape
+    if o is None:
+        o = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=q8.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q8.device)
+    qv, kv, vv, ov = _view8(q8, "q8"), _view8(k8, "k8"), _view8(v8, "v8"), _view(o, "o")
+    pq, pk, pv = (_f32_ptr(x, n, (B, H)) for x, n in ((q_amax, "q_amax"), (k_amax, "k_amax"), (v_amax, "v_amax")))
+    lp = _f32_ptr(lse, "lse", (B, H, S_q)) if lse is not None else None
+    st = lib().lsd_attn_fwd_fp8(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pq, pk, pv, ctypes.byref(ov),
+                                lp, ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q8))
+    _check(st, "lsd_attn_fwd_fp8")
     return (o, lse) if lse is not None else o
 
 

@@ -91,6 +91,32 @@ lsd_status check_view(const char* name, const lsd_view4* v) {
   return LSD_OK;
 }
 
+// Structural checks of an FP8 (one byte per element) view: the unit stride is
+// the channel stride (unit_dim 3) or, for V stored transposed, the sequence
+// stride (unit_dim 1); every other stride and the data pointer are multiples
+// of 16 bytes.
+lsd_status check_view8(const char* name, const lsd_view4* v, int unit_dim) {
+  if (v == nullptr) return fail(LSD_EINVAL, "%s: null view", name);
+  for (int i = 0; i < 4; ++i) {
+    if (v->shape[i] < 0) return fail(LSD_EINVAL, "%s: negative shape[%d]", name, i);
+    if (v->shape[i] > 0x7fffffff) return fail(LSD_EINVAL, "%s: shape[%d] exceeds 2^31-1", name, i);
+    if (v->stride[i] < 0) return fail(LSD_EINVAL, "%s: negative stride[%d]", name, i);
+  }
+  if (view_empty(*v)) return LSD_OK;
+  if (v->data == nullptr) return fail(LSD_EINVAL, "%s: null data pointer", name);
+  if (v->stride[unit_dim] != 1 && v->shape[unit_dim] > 1)
+    return fail(LSD_EINVAL, "%s: stride[%d] must be 1 (%s contiguous)", name, unit_dim,
+                unit_dim == 3 ? "head channels" : "tokens");
+  if ((uintptr_t)v->data % 16 != 0) return fail(LSD_EINVAL, "%s: data pointer not 16-byte aligned", name);
+  for (int i = 0; i < 4; ++i)
+    if (i != unit_dim && v->shape[i] > 1 && v->stride[i] % 16 != 0)
+      return fail(LSD_EINVAL, "%s: stride[%d]=%lld is not a multiple of 16 bytes", name, i, (long long)v->stride[i]);
+  double last = 0;
+  for (int i = 0; i < 4; ++i) last += (double)(v->shape[i] - 1) * (double)v->stride[i];
+  if (last > 9.0e18) return fail(LSD_EINVAL, "%s: view spans more than 2^62 bytes", name);
+  return LSD_OK;
+}
+
 bool same_shape(const lsd_view4& a, const lsd_view4& b) {
   for (int i = 0; i < 4; ++i)
     if (a.shape[i] != b.shape[i]) return false;
@@ -192,6 +218,113 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv; a.D = (int)D;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), acc ? "attn_fwd_accumulate" : "attn_fwd");
+}
+
+lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(LSD_EINVAL, "null src or dst array");
+  lsd_status s;
+  static const char* sn[3] = {"src[0] (q)", "src[1] (k)", "src[2] (v)"};
+  static const char* dn[3] = {"dst[0] (q8)", "dst[1] (k8)", "dst[2] (v8, transposed)"};
+  for (int t = 0; t < 3; ++t) {
+    if ((s = check_view(sn[t], &src[t])) != LSD_OK) return s;
+    if ((s = check_view8(dn[t], &dst[t], t == 2 ? 1 : 3)) != LSD_OK) return s;
+    if (!same_shape(src[t], src[0])) return fail(LSD_EINVAL, "%s: q, k and v must have one shape", sn[t]);
+    if (!same_shape(dst[t], src[0])) return fail(LSD_EINVAL, "%s: shape must equal the sources' (B, S, H, D)", dn[t]);
+  }
+  const int64_t B = src[0].shape[0], S = src[0].shape[1], H = src[0].shape[2], D = src[0].shape[3];
+  if (D != 128) return fail(LSD_EUNSUPPORTED, "FP8 path: head dim D=%lld unsupported (128)", (long long)D);
+  // V rows are written up to the next multiple of 64 tokens (zero codes)
+  const int64_t s_pad = (S + 63) / 64 * 64;
+  if (dst[2].stride[3] < s_pad)
+    return fail(LSD_EINVAL, "dst[2] (v8): row pitch stride[3]=%lld is below S=%lld rounded up to 64",
+                (long long)dst[2].stride[3], (long long)S);
+  if (amax == nullptr) return fail(LSD_EINVAL, "null amax");
+  if ((uintptr_t)amax % 4 != 0) return fail(LSD_EINVAL, "amax not 4-byte aligned");
+  if (B * H == 0) return ok();
+  Span ins[3], outs[4];
+  for (int t = 0; t < 3; ++t) {
+    ins[t] = span_of(src[t], 2);
+    outs[t] = span_of(dst[t], 1);
+  }
+  outs[2].hi += (uintptr_t)(s_pad - S);  // the last row's padding is written too
+  outs[3] = span_flat(amax, 3 * B * H, 4);
+  const char* on[4] = {dn[0], dn[1], dn[2], "amax"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], sn[j]);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], on[j]);
+  }
+  if ((s = check_device()) != LSD_OK) return s;
+  lsd::CastArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int t = 0; t < 3; ++t) {
+    a.src[t] = (const uint16_t*)src[t].data;
+    a.src_sb[t] = src[t].stride[0]; a.src_ss[t] = src[t].stride[1]; a.src_sh[t] = src[t].stride[2];
+    a.dst[t] = (uint8_t*)dst[t].data;
+    a.dst_sb[t] = dst[t].stride[0]; a.dst_ss[t] = dst[t].stride[1]; a.dst_sh[t] = dst[t].stride[2];
+  }
+  a.dst_sd_v = dst[2].stride[3];
+  a.amax = amax;
+  a.B = (int)B; a.S = (int)S; a.H = (int)H;
+  return launched(lsd::launch_cast_fp8(a, (hipStream_t)stream), "cast_qkv_fp8");
+}
+
+lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
+                        const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
+                        float softmax_scale, void* stream) {
+  lsd_status s;
+  if ((s = check_view8("q8", q8, 3)) != LSD_OK) return s;
+  if ((s = check_view8("k8", k8, 3)) != LSD_OK) return s;
+  if ((s = check_view8("v8 (transposed)", v8, 1)) != LSD_OK) return s;
+  if ((s = check_view("o", o)) != LSD_OK) return s;
+  const int64_t B = q8->shape[0], S_q = q8->shape[1], H = q8->shape[2], D = q8->shape[3];
+  const int64_t S_kv = k8->shape[1];
+  if (k8->shape[0] != B || k8->shape[2] != H || k8->shape[3] != D)
+    return fail(LSD_EINVAL, "k8 shape does not match q8 (B=%lld, H=%lld, D=%lld)", (long long)B, (long long)H,
+                (long long)D);
+  if (!same_shape(*v8, *k8)) return fail(LSD_EINVAL, "v8 shape must equal k8 shape (B, S_kv, H, D)");
+  if (!same_shape(*o, *q8)) return fail(LSD_EINVAL, "o shape must equal q8 shape (B, S_q, H, D)");
+  if (D != 128) return fail(LSD_EUNSUPPORTED, "FP8 path: head dim D=%lld unsupported (128)", (long long)D);
+  if (k8->stride[1] >= (int64_t(1) << 24) || v8->stride[3] >= (int64_t(1) << 24))
+    return fail(LSD_EUNSUPPORTED, "k8 sequence stride / v8 row pitch must be below 2^24 bytes");
+  if (S_kv > 0 && v8->stride[3] < (S_kv + 63) / 64 * 64)
+    return fail(LSD_EINVAL, "v8: row pitch stride[3]=%lld is below S_kv=%lld rounded up to 64",
+                (long long)v8->stride[3], (long long)S_kv);
+  if (q_amax == nullptr || k_amax == nullptr || v_amax == nullptr) return fail(LSD_EINVAL, "null amax array");
+  if ((uintptr_t)q_amax % 4 || (uintptr_t)k_amax % 4 || (uintptr_t)v_amax % 4)
+    return fail(LSD_EINVAL, "amax arrays not 4-byte aligned");
+  if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
+  if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
+  if (B * S_q * H == 0) return ok();
+  Span vs = span_of(*v8, 1);
+  if (S_kv > 0) vs.hi += (uintptr_t)((S_kv + 63) / 64 * 64 - S_kv);  // the padded tail of the last row
+  const Span ins[6] = {span_of(*q8, 1), span_of(*k8, 1), vs, span_flat(q_amax, B * H, 4),
+                       span_flat(k_amax, B * H, 4), span_flat(v_amax, B * H, 4)};
+  const Span so = span_of(*o, 2), sl = span_flat(lse, B * H * S_q, 4);
+  for (int j = 0; j < 6; ++j) {
+    if (overlaps(so, ins[j])) return fail(LSD_EINVAL, "o overlaps an input");
+    if (overlaps(sl, ins[j])) return fail(LSD_EINVAL, "lse overlaps an input");
+  }
+  if (overlaps(sl, so)) return fail(LSD_EINVAL, "lse overlaps o");
+  if ((s = check_device()) != LSD_OK) return s;
+
+  const float scale = (softmax_scale > 0.0f) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  lsd::AttnFp8Args a;
+  std::memset(&a, 0, sizeof a);
+  a.q = (const uint8_t*)q8->data;
+  a.k = (const uint8_t*)k8->data;
+  a.vt = (const uint8_t*)v8->data;
+  a.q_sb = q8->stride[0]; a.q_ss = q8->stride[1]; a.q_sh = q8->stride[2];
+  a.k_sb = k8->stride[0]; a.k_ss = k8->stride[1]; a.k_sh = k8->stride[2];
+  a.vt_sb = v8->stride[0]; a.vt_sh = v8->stride[2]; a.vt_sd = v8->stride[3];
+  a.q_amax = q_amax; a.k_amax = k_amax; a.v_amax = v_amax;
+  a.o = (uint16_t*)o->data;
+  a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2];
+  a.lse = lse;
+  a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  return launched(lsd::launch_attn_fp8(a, (hipStream_t)stream), "attn_fwd_fp8");
 }
 
 }  // namespace
@@ -355,6 +488,16 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
 }  // namespace
 
 extern "C" {
+
+lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream) {
+  return cast_qkv_fp8(src, dst, amax, stream);
+}
+
+lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
+                            const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
+                            float softmax_scale, void* stream) {
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o, lse, softmax_scale, stream);
+}
 
 lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,
                                     void* stream) {

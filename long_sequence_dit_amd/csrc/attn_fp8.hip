@@ -1,0 +1,368 @@
+// Dense bidirectional attention forward on FP8 (E4M3) inputs, for gfx950.
+//
+// Computes the attention of the dequantised inputs q = code_q * s_q,
+// k = code_k * s_k, v = code_v * s_v (s = amax / 448 per (b, h), as the FP8
+// cast produces them): per query row, LSE = ln sum_j exp(scale q.k_j) and
+// O = sum_j exp(scale q.k_j - LSE) v_j, O rounded to bf16
+// ("Scaling Video Generation Across NVL72 rack with TensorRT-LLM", "Ulysses
+// Parallelism > Fused vs. unfused QKV all-to-all": FP8 inputs for the
+// attention kernel, produced by one cast of the stacked QKV; "The Scaling
+// Challenge in Video Generation": dense, unmasked attention).
+//
+// The structure follows the bf16 kernel (8 waves, 256 query rows per
+// workgroup, 64-key tiles double-buffered in LDS, the two waves of a SIMD
+// alternating MFMA and softmax phases); the products run on
+// v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 rate).  In that instruction
+// lane l (row or column l % 32) holds 32 codes of the 64-long reduction for
+// lane half l / 32, and only the pairing of A and B matters, so the kernel
+// chooses the reduction order:
+// * QK^T: S^T = K Q^T, reduction over channels; lane half hh holds channels
+//   [64 s + 32 hh, +32) of step s in both operands.
+// * K rows are stored in LDS permuted (row 8 (r/4) + 4 hh + r % 4 of a 32-key
+//   block holds key 16 hh + r), so accumulator register r of lane half hh is
+//   the score of key 16 hh + r: each lane half holds 16 consecutive keys.
+// * PV: O^T = V^T P^T, reduction over the tile's 64 keys; byte j of lane half
+//   hh is key 32 (j / 16) + 16 hh + j % 16.  The softmax weights, converted to
+//   E4M3 in accumulator order, are the B operand as they stand, and the A
+//   operand is two 16-byte pieces of a V^T row (V arrives transposed, keys
+//   contiguous, from the cast).
+// * The dequantisation factors fold into the softmax scale (s_q s_k) and the
+//   final normalisation (s_v / l); weights are <= 2^8 (lazy rescaling), well
+//   inside E4M3's range of 448.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsd_internal.h"
+
+namespace lsd {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlockM = kWaves * 32;       // query rows per workgroup
+constexpr int kBlockN = 64;                // keys per LDS tile
+constexpr float kRescaleThreshold = 8.0f;  // log2 units; keeps weights <= 2^8
+constexpr int kRowK = D + 16;              // K row pitch (bytes): 16-byte skew per row
+constexpr int kRowV = kBlockN + 16;        // V^T row pitch (bytes)
+constexpr int kLdsK = kBlockN * kRowK;     // bytes per K buffer
+constexpr int kLdsV = D * kRowV;           // bytes per V^T buffer
+constexpr int kRowO = D + 4;               // output staging pitch (bf16 elements)
+constexpr int kLdsO = kWaves * 32 * kRowO * 2;
+constexpr int kLds = (2 * (kLdsK + kLdsV) > kLdsO) ? 2 * (kLdsK + kLdsV) : kLdsO;
+
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// four float32 values -> four E4M3 codes (byte i = value i), nearest even
+__device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+__device__ inline float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+__device__ inline float partner_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ inline float partner_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ inline f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// LDS row of key kk (0..63) in a K tile: within each 32-key block, key
+// 16 hh + r sits in row 8 (r / 4) + 4 hh + r % 4.
+__device__ inline int k_lds_row(int kk) {
+  const int x = kk & 31;
+  return (kk & 32) + 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3);
+}
+
+__global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a, int n_qtiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  uint8_t* Ks = smem;               // [2][64][kRowK] bytes, rows permuted
+  uint8_t* Vs = smem + 2 * kLdsK;   // [2][D][kRowV] bytes, V^T
+
+  // XCD-aware tile order, batch index fastest (as in the bf16 kernel).
+  const int nblk = gridDim.x;
+  const int pid = blockIdx.x;
+  const int xcd = pid & 7;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int logical = xcd * per + min(xcd, rem) + (pid >> 3);
+  const int qt = logical % n_qtiles;
+  const int hb = logical / n_qtiles;
+  const int b = hb % a.B;
+  const int h = hb / a.B;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int skv = a.S_kv;  // >= 1 here
+  const int n_tiles = (skv + kBlockN - 1) / kBlockN;
+  const float s_q = a.q_amax[b * a.H + h] / 448.0f;
+  const float s_k = a.k_amax[b * a.H + h] / 448.0f;
+  const float s_v = a.v_amax[b * a.H + h] / 448.0f;
+  const float c = a.scale_log2 * s_q * s_k;
+
+  // ---- Q rows of this wave: 32 codes per lane per 64-channel step.
+  const int qrow = qt * kBlockM + wave * 32 + l32;
+  const bool qvalid = qrow < a.S_q;
+  i32x8 qreg[2];
+  {
+    const uint8_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)min(qrow, a.S_q - 1) * a.q_ss +
+                        (int64_t)h * a.q_sh + 32 * hh;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 lo = *(const u32x4*)(qp + 64 * s);
+      u32x4 hi = *(const u32x4*)(qp + 64 * s + 16);
+      if (!qvalid) lo = hi = (u32x4){0u, 0u, 0u, 0u};
+      qreg[s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  }
+
+  // ---- staging: each thread moves one 16-byte piece of K and of V^T per tile,
+  // through buffer loads with a per-tile descriptor.  K rows past the last key
+  // read as zero (their scores are masked); V^T rows are padded to a multiple
+  // of 64 tokens, so a tile never leaves its rows.
+  const uint8_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const uint8_t* vbase = a.vt + (int64_t)b * a.vt_sb + (int64_t)h * a.vt_sh;
+  const int k_key = tid >> 3, k_ch = tid & 7;
+  const uint32_t k_off = (uint32_t)(k_key * a.k_ss + 16 * k_ch);
+  const int k_dst = k_lds_row(k_key) * kRowK + 16 * k_ch;
+  const int v_d = tid >> 2, v_q = tid & 3;
+  const uint32_t v_off = (uint32_t)(v_d * a.vt_sd + 16 * v_q);
+  const int v_dst = v_d * kRowV + 16 * v_q;
+  const int v_range = (int)((D - 1) * a.vt_sd + kBlockN);
+  u32x4 kst, vst;
+  auto load_k = [&](int t) {
+    const int64_t rows = (int64_t)skv - (int64_t)t * kBlockN;
+    const int64_t any = -(int64_t)(rows > 0);
+    const int n = (int)(((min(rows, (int64_t)kBlockN) - 1) * a.k_ss + D) & any);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t * kBlockN * a.k_ss), (short)0, n, 0x00020000);
+    kst = __builtin_amdgcn_raw_buffer_load_b128(r, k_off, 0, 0);
+  };
+  auto load_v = [&](int t) {
+    const int n = (t < n_tiles) ? v_range : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t * kBlockN), (short)0, n, 0x00020000);
+    vst = __builtin_amdgcn_raw_buffer_load_b128(r, v_off, 0, 0);
+  };
+  auto store_k = [&](int t) { *(u32x4*)(Ks + (t & 1) * kLdsK + k_dst) = kst; };
+  auto store_v = [&](int t) { *(u32x4*)(Vs + (t & 1) * kLdsV + v_dst) = vst; };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  f32x16 sacc[2];
+  uint32_t pk[8];  // this tile's weights as E4M3, in PV operand order
+
+  auto mask_tail = [&](int t) {
+    const int kv0 = t * kBlockN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv0 + 32 * kb + 16 * hh + r >= skv) sacc[kb][r] = -INFINITY;
+  };
+  auto softmax = [&]() {
+    float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) {
+      mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
+      mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+    }
+    float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+    mx = partner_max(mx) * c;
+    const float m_new = vmax(m_run, mx);
+    const bool need = m_new > m_run + kRescaleThreshold;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float lt0 = 0.0f, lt1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r = 4 * (w & 3);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 0], c, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 2], c, neg_m));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 3], c, neg_m));
+      lt0 += p0 + p2;
+      lt1 += p1 + p3;
+      pk[w] = pack4_fp8(p0, p1, p2, p3);
+    }
+    l_run += lt0 + lt1;
+  };
+
+  // ---- MFMA phase: PV(t) on 4 d-blocks, then QK(t+1) on 2 key blocks x 2
+  // channel steps.  Each step's A operand is two 16-byte LDS reads, issued two
+  // steps ahead; sched_barrier fences keep the order.
+  constexpr int kSteps = 8;
+  constexpr int kDist = 2;
+  auto frag_off = [&](int i, int t) -> const uint8_t* {
+    if (i < 4)  // V^T rows 32 db + l32, keys [16 hh, +16) and [32 + 16 hh, +16)
+      return Vs + (t & 1) * kLdsV + (32 * i + l32) * kRowV + 16 * hh;
+    const int j = i - 4, kb = j >> 1, s = j & 1;
+    return Ks + ((t + 1) & 1) * kLdsK + (32 * kb + l32) * kRowK + 64 * s + 32 * hh;
+  };
+  auto frag_load = [&](int i, int t) -> i32x8 {
+    const uint8_t* p = frag_off(i, t);
+    const u32x4 lo = *(const u32x4*)p;
+    const u32x4 hi = *(const u32x4*)(p + (i < 4 ? 32 : 16));
+    return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto mfma_phase = [&](int t) {
+    i32x8 fr[kDist];
+#pragma unroll
+    for (int i = 0; i < kDist; ++i) fr[i] = frag_load(i, t);
+    const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const i32x8 cur = fr[i % kDist];
+      if (i + kDist < kSteps) fr[i % kDist] = frag_load(i + kDist, t);
+      if (i < 4) {
+        oacc[i] = mfma_fp8(cur, pb, oacc[i]);
+      } else {
+        const int j = i - 4, kb = j >> 1, s = j & 1;
+        sacc[kb] = mfma_fp8(cur, qreg[s], s == 0 ? (f32x16){} : sacc[kb]);
+      }
+      if (i == 1) store_k(t + 2);
+      if (i == 2) store_v(t + 1);
+      if (i == 4) load_k(t + 3);
+      if (i == 5) load_v(t + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- ping-pong schedule (as in the bf16 kernel): group A (waves 0-3) runs
+  // one barrier interval ahead of group B (waves 4-7).
+  const int group = wave >> 2;
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
+  __syncthreads();
+  load_k(2);
+  load_v(1);
+  {  // QK(0)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = (f32x16){};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint8_t* p = Ks + (32 * kb + l32) * kRowK + 64 * s + 32 * hh;
+        const u32x4 lo = *(const u32x4*)p;
+        const u32x4 hi = *(const u32x4*)(p + 16);
+        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        sacc[kb] = mfma_fp8(kf, qreg[s], sacc[kb]);
+      }
+    }
+  }
+  if (group == 1) lds_barrier();
+  for (int t = 0; t < n_tiles; ++t) {
+    if ((t + 1) * kBlockN > skv) mask_tail(t);
+    softmax();
+    lds_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase(t);
+    __builtin_amdgcn_s_setprio(0);
+    lds_barrier();
+  }
+  if (group == 0) lds_barrier();
+
+  // ---- epilogue: O = s_v O^T / l, LSE = ln 2 (m + log2 l), O staged through LDS
+  const float l_tot = partner_sum(l_run);
+  const float osc = s_v / l_tot;
+  __syncthreads();
+  uint16_t* Ow = (uint16_t*)smem + wave * 32 * kRowO;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * osc, oacc[db][4 * g + 1] * osc),
+                       pack_bf16(oacc[db][4 * g + 2] * osc, oacc[db][4 * g + 3] * osc)};
+      *(u32x2*)(Ow + l32 * kRowO + 32 * db + 8 * g + 4 * hh) = w;
+    }
+  if (a.lse != nullptr && hh == 0 && qvalid)
+    a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  constexpr int kCPR = D / 8;
+  constexpr int kRowsPerPass = 64 / kCPR;
+  const int ch = lane % kCPR;
+  const int r0 = lane / kCPR;
+  const int row_base = qt * kBlockM + wave * 32;
+  uint16_t* obase = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 8 * ch;
+#pragma unroll
+  for (int r = r0; r < 32; r += kRowsPerPass) {
+    const u32x4 v = *(const u32x4*)(Ow + r * kRowO + 8 * ch);
+    const int row = row_base + r;
+    if (row < a.S_q) *(u32x4*)(obase + (int64_t)row * a.o_ss) = v;
+  }
+}
+
+// S_kv == 0: O = 0, LSE = -inf.
+__global__ void attn_fp8_empty_kernel(const AttnFp8Args a) {
+  const int64_t n = (int64_t)a.B * a.S_q * a.H * (D / 8);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % (D / 8));
+    const int64_t row = i / (D / 8);
+    const int h = (int)(row % a.H);
+    const int64_t bs = row / a.H;
+    const int s = (int)(bs % a.S_q);
+    const int b = (int)(bs / a.S_q);
+    *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = (u32x4){0u, 0u, 0u, 0u};
+    if (a.lse != nullptr && c == 0) a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp8(const AttnFp8Args& a, hipStream_t stream) {
+  if (a.S_kv == 0) {
+    const int64_t n = (int64_t)a.B * a.S_q * a.H * (D / 8);
+    const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+    hipLaunchKernelGGL(attn_fp8_empty_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
+  const int64_t nblk = (int64_t)n_qtiles * a.H * a.B;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace lsd

@@ -1,0 +1,164 @@
+// Single-pass FP8 cast of Q, K, V for the FP8 attention path, gfx950.
+//
+// ("Scaling Video Generation Across NVL72 rack with TensorRT-LLM", "Ulysses
+// Parallelism > Fused vs. unfused QKV all-to-all": the stacked QKV buffer gets
+// one FP8 cast before the attention kernel, in a layout the kernel reads
+// without another copy.)
+//
+// Per (tensor t, batch b, head h): amax = max |x| over tokens and channels;
+// code = E4M3(x * (448 / amax)) with the product rounded to float32 and the
+// code rounded to nearest even (v_cvt_pk_fp8_f32); amax == 0 uses factor 1.
+// Q and K keep their (B, S, H, D) layout; V is written transposed, keys
+// contiguous per (b, h, d), which is the operand layout of the PV product.
+//
+// Three launches on the caller's stream: clear amax, reduce it (integer max
+// on the float bits of non-negative values: order-independent, so the result
+// is deterministic), then quantise.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsd_internal.h"
+
+namespace lsd {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 64;  // tokens per wave (amax, Q/K) or per workgroup (V)
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// four float32 values -> four E4M3 codes in one dword (byte i = value i)
+__device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+__global__ void amax_clear_kernel(float* amax, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) amax[i] = 0.0f;
+}
+
+// One wave per (t, b, h, chunk of 64 tokens); each pass covers 4 tokens x 256 B
+// (16 lanes per token row of D = 128 channels).
+__global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)3 * a.B * a.H * n_chunks;
+  if (w >= n_waves) return;
+  const int chunk = (int)(w % n_chunks);
+  const int64_t tbh = w / n_chunks;
+  const int h = (int)(tbh % a.H);
+  const int b = (int)((tbh / a.H) % a.B);
+  const int t = (int)(tbh / ((int64_t)a.H * a.B));
+  const uint16_t* base = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t];
+  const int vec = lane & 15;   // 16-byte vector within the 256-byte row
+  float m = 0.0f;
+  for (int i = lane >> 4; i < kChunk; i += 4) {
+    const int s = chunk * kChunk + i;
+    if (s < a.S) {
+      const u32x4 x = *(const u32x4*)(base + (int64_t)s * a.src_ss[t] + 8 * vec);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[e])), fabsf(bf16_hi(x[e]))));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) atomicMax((unsigned int*)&a.amax[((int64_t)t * a.B + b) * a.H + h], __float_as_uint(m));
+}
+
+__device__ inline float inv_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 1.0f; }
+
+// Q and K: one wave per (t in {0,1}, b, h, 64 tokens); 16-byte bf16 vectors in,
+// 8-byte code vectors out.
+__global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)2 * a.B * a.H * n_chunks;
+  if (w >= n_waves) return;
+  const int chunk = (int)(w % n_chunks);
+  const int64_t tbh = w / n_chunks;
+  const int h = (int)(tbh % a.H);
+  const int b = (int)((tbh / a.H) % a.B);
+  const int t = (int)(tbh / ((int64_t)a.H * a.B));
+  const float inv = inv_scale(a.amax[((int64_t)t * a.B + b) * a.H + h]);
+  const uint16_t* src = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t];
+  uint8_t* dst = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)h * a.dst_sh[t];
+  const int vec = lane & 15;
+  for (int i = lane >> 4; i < kChunk; i += 4) {
+    const int s = chunk * kChunk + i;
+    if (s < a.S) {
+      const u32x4 x = *(const u32x4*)(src + (int64_t)s * a.src_ss[t] + 8 * vec);
+      u32x2 c;
+      c[0] = pack4_fp8(bf16_lo(x[0]) * inv, bf16_hi(x[0]) * inv, bf16_lo(x[1]) * inv, bf16_hi(x[1]) * inv);
+      c[1] = pack4_fp8(bf16_lo(x[2]) * inv, bf16_hi(x[2]) * inv, bf16_lo(x[3]) * inv, bf16_hi(x[3]) * inv);
+      *(u32x2*)(dst + (int64_t)s * a.dst_ss[t] + 8 * vec) = c;
+    }
+  }
+}
+
+// V: one workgroup per (b, h, 64 tokens).  Thread (token group g of 4 tokens,
+// channel chunk c of 8 channels) converts a 4 x 8 block and writes, for each
+// of its 8 channels, the 4 tokens' codes as one dword of the transposed tile
+// in LDS ([d][64 tokens], pitch 80 B); then the tile leaves as 16-byte row
+// pieces.  Rows are padded to a multiple of 64 tokens: the last tile writes
+// zero codes for tokens S .. (its end), so every 64-token tile of a row is
+// readable and finite.
+__global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 80];
+  const int chunk = blockIdx.x % n_chunks;
+  const int bh = blockIdx.x / n_chunks;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const float inv = inv_scale(a.amax[((int64_t)2 * a.B + b) * a.H + h]);
+  const uint16_t* src = a.src[2] + (int64_t)b * a.src_sb[2] + (int64_t)h * a.src_sh[2];
+  const int s0 = chunk * kChunk;
+  const int tid = threadIdx.x;
+  const int g = tid >> 4;      // token group (0..15)
+  const int c = tid & 15;      // channel chunk (0..15)
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = s0 + 4 * g + i;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (s < a.S) x = *(const u32x4*)(src + (int64_t)s * a.src_ss[2] + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[i][2 * e] = bf16_lo(x[e]) * inv;
+      v[i][2 * e + 1] = bf16_hi(x[e]) * inv;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    *(uint32_t*)(tile + (8 * c + e) * 80 + 4 * g) = pack4_fp8(v[0][e], v[1][e], v[2][e], v[3][e]);
+  __syncthreads();
+  // 128 rows x 4 pieces of 16 bytes; 2 per thread
+  uint8_t* dst = a.dst[2] + (int64_t)b * a.dst_sb[2] + (int64_t)h * a.dst_sh[2];
+  for (int p = tid; p < 128 * 4; p += 256) {
+    const int d = p >> 2, q = p & 3;
+    const u32x4 val = *(const u32x4*)(tile + d * 80 + 16 * q);   // tokens >= S were loaded as 0
+    *(u32x4*)(dst + (int64_t)d * a.dst_sd_v + s0 + 16 * q) = val;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t stream) {
+  const int n = 3 * a.B * a.H;
+  hipLaunchKernelGGL(amax_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.amax, n);
+  if (a.S == 0) return hipGetLastError();
+  const int n_chunks = (a.S + kChunk - 1) / kChunk;
+  const int64_t amax_waves = (int64_t)3 * a.B * a.H * n_chunks;
+  const int64_t qk_waves = (int64_t)2 * a.B * a.H * n_chunks;
+  const int64_t vt_blocks = (int64_t)a.B * a.H * n_chunks;
+  if ((amax_waves + 3) / 4 > 0x7fffffff || vt_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)((amax_waves + 3) / 4)), dim3(256), 0, stream, a, n_chunks);
+  hipLaunchKernelGGL(quant_qk_kernel, dim3((unsigned)((qk_waves + 3) / 4)), dim3(256), 0, stream, a, n_chunks);
+  hipLaunchKernelGGL(quant_vt_kernel, dim3((unsigned)vt_blocks), dim3(256), 0, stream, a, n_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace lsd

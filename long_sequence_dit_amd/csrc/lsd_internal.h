@@ -65,4 +65,41 @@ struct RelayoutArgs {
 int64_t relayout_runs(const RelayoutArgs& a);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream);
 
+// FP8 cast of Q, K, V (D = 128).  Sources are bf16 (B, S, H, D) views; dst[0]
+// and dst[1] are E4M3 (B, S, H, D) views (byte strides, channels contiguous);
+// dst[2] is V transposed: element (b, s, h, d) at dst[2] + b*dst_sb[2] +
+// h*dst_sh[2] + d*dst_sd_v + s.
+struct CastArgs {
+  const uint16_t* src[3];
+  int64_t src_sb[3], src_ss[3], src_sh[3];
+  uint8_t* dst[3];
+  int64_t dst_sb[3], dst_ss[3], dst_sh[3];
+  int64_t dst_sd_v;
+  float* amax;  // [3, B, H]
+  int B, S, H;
+};
+hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t stream);
+
+// FP8 attention (D = 128).  q, k: E4M3 (B, S, H, D) views with byte strides;
+// vt: V transposed, element (b, s, h, d) at vt + b*vt_sb + h*vt_sh + d*vt_sd
+// + s, rows readable up to S_kv rounded up to 64 tokens.  amax arrays are
+// [B, H]; the dequantisation factor is amax / 448.
+struct AttnFp8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* vt;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t vt_sb, vt_sh, vt_sd;
+  const float* q_amax;
+  const float* k_amax;
+  const float* v_amax;
+  uint16_t* o;
+  int64_t o_sb, o_ss, o_sh;
+  float* lse;  // [B, H, S_q], may be null
+  int B, H, S_q, S_kv;
+  float scale_log2;
+};
+hipError_t launch_attn_fp8(const AttnFp8Args& a, hipStream_t stream);
+
 }  // namespace lsd

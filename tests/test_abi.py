@@ -238,6 +238,60 @@ def test_attn_fwd_masked_and_accumulate_validation():
     assert r == LSD_EINVAL and "overlaps" in L.lsd_last_error().decode()
 
 
+def view8(addr, shape, stride):
+    return view(addr, shape, stride)
+
+
+def test_fp8_cast_and_attention_validation():
+    L = lsd.lib()
+    B, S, H, D = 2, 100, 3, 128
+    bf = [view(BASE + t * GB, (B, S, H, D)) for t in range(3)]
+    s_pad = 128
+    q8 = view8(BASE + 10 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    k8 = view8(BASE + 11 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    v8 = view8(BASE + 12 * GB, (B, S, H, D), [H * D * s_pad, 1, D * s_pad, s_pad])
+    amax = BASE + 13 * GB
+
+    def cast(src, dst, am):
+        r = L.lsd_cast_qkv_fp8((View4 * 3)(*src), (View4 * 3)(*dst), ctypes.c_void_p(am) if am else None, None)
+        return r, L.lsd_last_error().decode()
+
+    r, msg = cast(bf, [q8, k8, view8(BASE + 12 * GB, (B, S, H, D), [H * D * 112, 1, D * 112, 112])], amax)
+    assert r == LSD_EINVAL and "rounded up to 64" in msg
+    r, msg = cast(bf, [q8, k8, view8(BASE + 12 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])], amax)
+    assert r == LSD_EINVAL and "stride[1] must be 1" in msg
+    r, msg = cast([view(BASE + t * GB, (B, S, H, 64)) for t in range(3)],
+                  [view8(BASE + (10 + t) * GB, (B, S, H, 64), [S * H * 64, H * 64, 64, 1]) for t in range(2)]
+                  + [view8(BASE + 12 * GB, (B, S, H, 64), [H * 64 * s_pad, 1, 64 * s_pad, s_pad])], amax)
+    assert r == LSD_EUNSUPPORTED and "128" in msg
+    r, msg = cast(bf, [q8, k8, v8], 0)
+    assert r == LSD_EINVAL and "amax" in msg
+    r, msg = cast(bf, [q8, q8, v8], amax)
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = cast(bf, [q8, k8, v8], BASE + 12 * GB + 64)
+    assert r == LSD_EINVAL and "overlaps" in msg
+
+    o = view(BASE + 20 * GB, (B, S, H, D))
+
+    def attn8(qv, kv, vv, ov, lse=None, amaxes=(amax, amax + 64, amax + 128)):
+        a = [ctypes.c_void_p(x) if x else None for x in amaxes]
+        r = L.lsd_attn_fwd_fp8(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), a[0], a[1], a[2],
+                               ctypes.byref(ov), None if lse is None else ctypes.c_void_p(lse),
+                               ctypes.c_float(0.0), None)
+        return r, L.lsd_last_error().decode()
+
+    r, msg = attn8(q8, k8, view8(BASE + 12 * GB, (B, S, H, D), [H * D * 96, 1, D * 96, 96]), o)
+    assert r == LSD_EINVAL and "rounded up to 64" in msg
+    r, msg = attn8(q8, k8, v8, o, amaxes=(amax, 0, amax))
+    assert r == LSD_EINVAL and "amax" in msg
+    r, msg = attn8(q8, k8, v8, view(BASE + 12 * GB + 4096, (B, S, H, D)))
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = attn8(q8, k8, v8, o, lse=BASE + 10 * GB + 32)
+    assert r == LSD_EINVAL and "overlaps" in msg
+    r, msg = attn8(q8, view8(BASE + 11 * GB, (B, S, H + 1, D), [S * (H + 1) * D, (H + 1) * D, D, 1]), v8, o)
+    assert r == LSD_EINVAL and "k8 shape" in msg
+
+
 def test_attn_fwd_rejects_huge_kv_stride():
     q, k, v, o = good4()
     k = view(BASE + GB, (1, 256, 2, 64), [256 * (1 << 24), 1 << 24, 64, 1])

@@ -1,0 +1,159 @@
+"""The FP8 path on the GPU (through the C ABI): the cast of Q, K, V to E4M3
+bit-exact against the oracle (codes and amax), and FP8 attention against the
+oracle's attention of the dequantised inputs within the FP8 contract:
+
+  per element  |O - O_ref| <= 2^-4 A + 2^-10 C + 2^-8 |O_ref| + 1e-5
+  overall      mean |O - O_ref| <= 0.05 mean |O_ref| + 1e-4
+  LSE          |LSE - LSE_ref| <= 1e-3
+
+with A = sum_j p_j |v_j| / l and C = sum_j |v_j| / l (p_j = exp(s_j - max s),
+l = sum p): the E4M3 weights carry at most half an ulp (2^-4) of relative
+error, or 2^-10 absolute below the normal range; the bf16 output adds 2^-9
+relative.  The logits are exact FP8 products summed in float32, so the LSE
+keeps the bf16 path's bar."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import fp8, ref
+from gpu_util import note, to_dev, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+lsd = pytest.importorskip("long_sequence_dit_amd")
+
+
+def codes(x):
+    t = torch()
+    return np.ascontiguousarray(x.view(t.uint8).cpu().numpy())
+
+
+def deq_rows(c, amax, b, h, rows=None):
+    s = float(np.float32(np.float32(amax[b, h]) / np.float32(448.0)))
+    x = c[b, :, h, :] if rows is None else c[b, rows, h, :]
+    return fp8.e4m3_decode(x) * s
+
+
+def check_fp8(o, lse, q8, k8, v8, amax, heads, rows_fn, what, scale=None):
+    """o, lse on the GPU; q8/k8/v8 host codes (B, S, H, D); amax [3, B, H]."""
+    og = to_f64(o)
+    lg = lse.cpu().numpy()
+    D = q8.shape[3]
+    sc = ref._default_scale(D, scale)
+    worst = 0.0
+    errs, mags = [], []
+    for b in range(q8.shape[0]):
+        for h in heads:
+            rows = rows_fn(b, h)
+            qh = deq_rows(q8, amax[0], b, h, rows)
+            kh = deq_rows(k8, amax[1], b, h)
+            vh = deq_rows(v8, amax[2], b, h)
+            O, L = ref._attend_block(qh, kh, vh, sc)
+            if kh.shape[0] == 0:
+                assert np.all(og[b, rows, h] == 0) and np.all(np.isneginf(lg[b, h, rows])), what
+                continue
+            s = (qh @ kh.T) * sc
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            l = p.sum(axis=1, keepdims=True)
+            A = (p @ np.abs(vh)) / l
+            C = np.abs(vh).sum(axis=0)[None, :] / l
+            bound = 2.0 ** -4 * A + 2.0 ** -10 * C + 2.0 ** -8 * np.abs(O) + 1e-5
+            err = np.abs(og[b, rows, h] - O)
+            assert np.all(np.isfinite(og[b, rows, h])), f"{what} b={b} h={h}: non-finite"
+            ratio = float((err / bound).max())
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"{what} b={b} h={h}: error exceeds the FP8 bound (ratio {ratio:.3f})"
+            dl = np.abs(lg[b, h, rows] - L)
+            assert dl.max() <= 1e-3, f"{what} b={b} h={h}: LSE max-abs {dl.max():.3e}"
+            errs.append(err.ravel())
+            mags.append(np.abs(O).ravel())
+    if errs:
+        e, m = np.concatenate(errs), np.concatenate(mags)
+        assert e.mean() <= 0.05 * m.mean() + 1e-4, f"{what}: mean-abs {e.mean():.3e} vs mean|O| {m.mean():.3e}"
+        note(f"{what}: worst bound ratio {worst:.3f}, mean-abs {e.mean():.3e} ({e.mean() / max(m.mean(), 1e-30):.2%} "
+             f"of mean |O|)")
+
+
+def all_rows(S):
+    return lambda b, h: np.arange(S)
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 3), (1, 64, 2), (1, 1, 1), (2, 257, 2)])
+def test_cast_bit_exact(shape):
+    B, S, H = shape
+    note(f"fp8 cast B={B} S={S} H={H}")
+    t = torch()
+    q = synth.normal_bf16((B, S, H, 128), 100, 1)
+    k = synth.normal_bf16((B, S, H, 128), 101, 1).copy()
+    v = synth.normal_bf16((B, S, H, 128), 102, 1).copy()
+    k[0, :, H - 1] = 0                                           # an all-zero head
+    v[B - 1, :, 0] = synth.f32_to_bf16_bits(ref.bf16_bits_to_f64(v[B - 1, :, 0]).astype(np.float32) * 300)
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(to_dev(q), to_dev(k), to_dev(v))
+    t.cuda.synchronize()
+    eq8, ek8, ev8, eamax = fp8.cast_qkv(q, k, v)
+    assert np.array_equal(amax.cpu().numpy(), eamax), "amax"
+    assert np.array_equal(codes(q8), eq8), "q codes"
+    assert np.array_equal(codes(k8), ek8), "k codes"
+    assert np.array_equal(codes(v8), ev8), "v codes (transposed storage)"
+    # the transposed rows are zero-padded up to a multiple of 64 tokens
+    store = v8.as_strided((B, H, 128, (S + 63) // 64 * 64), (v8.stride(0), v8.stride(2), v8.stride(3), 1))
+    pad = codes(store)[..., S:]
+    assert pad.size == 0 or np.all(pad == 0), "v padding"
+
+
+def test_cast_from_fused_strided_views():
+    note("fp8 cast from a fused [B,S,3,H,D] buffer")
+    t = torch()
+    fused = synth.normal_bf16((2, 150, 3, 4, 128), 103, 1)
+    f = to_dev(fused)
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(f[:, :, 0], f[:, :, 1], f[:, :, 2])
+    t.cuda.synchronize()
+    eq8, ek8, ev8, eamax = fp8.cast_qkv(fused[:, :, 0], fused[:, :, 1], fused[:, :, 2])
+    assert np.array_equal(amax.cpu().numpy(), eamax)
+    assert np.array_equal(codes(q8), eq8) and np.array_equal(codes(k8), ek8) and np.array_equal(codes(v8), ev8)
+
+
+@pytest.mark.parametrize("S_q,S_kv", [(300, 333), (256, 64), (200, 1), (70, 640), (512, 257)])
+def test_attention_within_fp8_contract(S_q, S_kv):
+    note(f"fp8 attention S_q={S_q} S_kv={S_kv}")
+    t = torch()
+    B, H = 2, 3
+    q = synth.normal_bf16((B, S_q, H, 128), 104, 1)
+    k = synth.normal_bf16((B, S_kv, H, 128), 105, 1)
+    v = synth.normal_bf16((B, S_kv, H, 128), 106, 1)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    q8, _, _, aq = lsd.cast_qkv_fp8(dq, dq, dq)
+    _, k8, v8, akv = lsd.cast_qkv_fp8(dk, dk, dv)
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, aq[0], akv[1], akv[2])
+    t.cuda.synchronize()
+    amax = np.stack([aq[0].cpu().numpy(), akv[1].cpu().numpy(), akv[2].cpu().numpy()])
+    check_fp8(o, lse, codes(q8), codes(k8), codes(v8), amax, range(H), all_rows(S_q), f"fp8 {S_q}x{S_kv}")
+    # for context only: distance to bf16 attention of the unquantised inputs
+    O, _ = ref.attention(q, k, v)
+    d = np.abs(to_f64(o) - O)
+    note(f"  vs unquantised inputs: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+
+
+def test_outlier_keys_empty_block_and_ring_slice():
+    note("fp8 attention: outlier keys, S_kv = 0, 64-aligned key block of the padded V rows")
+    t = torch()
+    q, k, v, _ = synth.cosmos_qkv(seed=4, S=2000, H=2, D=128)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(dq, dk, dv)
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    a = amax.cpu().numpy()
+    hq, hk, hv = codes(q8), codes(k8), codes(v8)
+    check_fp8(o, lse, hq, hk, hv, a, range(2), all_rows(2000), "fp8 outliers")
+    # a key block [640, 1400) of the same FP8 tensors, as a Ring step would use
+    o2, l2 = lsd.attn_fwd_fp8(q8, k8[:, 640:1400], v8[:, 640:1400], amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    check_fp8(o2, l2, hq, hk[:, 640:1400], hv[:, 640:1400], a, range(2), all_rows(2000), "fp8 key block")
+    o3, l3 = lsd.attn_fwd_fp8(q8, k8[:, :0], v8[:, :0], amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    assert (o3.float() == 0).all() and t.isneginf(l3).all()
+    # determinism
+    o4, l4 = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    assert t.equal(o4.view(t.int16), o.view(t.int16)) and t.equal(l4, lse)

@@ -66,6 +66,22 @@ def test_ltx2_scale_key_padding_mask():
     check_rows(o, lse, q, k[:, :n], v[:, :n], range(0, 32, 5), 11, "LTX-2 masked")
 
 
+def test_ltx2_scale_fp8():
+    note("full LTX-2 on the FP8 path: cast + FP8 attention, B=1 S=24576 H=32")
+    from test_fp8_gpu import check_fp8, codes
+    t = torch()
+    q, k, v = synth.ltx2_qkv()
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(to_dev(q), to_dev(k), to_dev(v))
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    from oracle import fp8 as ofp8
+    eq8, ek8, ev8, eamax = ofp8.cast_qkv(q, k, v)
+    hq, hk, hv = codes(q8), codes(k8), codes(v8)
+    assert np.array_equal(amax.cpu().numpy(), eamax) and np.array_equal(hq, eq8)
+    assert np.array_equal(hk, ek8) and np.array_equal(hv, ev8)
+    check_fp8(o, lse, hq, hk, hv, eamax, range(0, 32, 3), lambda b, h: sample_rows(24576, 300 + h), "LTX-2 fp8")
+
+
 def test_wan_ulysses_share_relayout_then_attention():
     note("full Wan Ulysses share: fused QKV [2,75600,3,40,128] -> rank slices, P=4")
     t = torch()
