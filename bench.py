@@ -246,9 +246,9 @@ class Pipeline:
         return 2 * len(self.kernel_names())
 
 
-def kernel_source_hash():
+def kernel_source_hash(name):
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "long_sequence_dit_amd", "csrc", "attn_fwd.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "long_sequence_dit_amd", "csrc", name), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -262,7 +262,8 @@ def load_traffic(workload):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("attn_fwd_source_sha256_16") != kernel_source_hash():
+    src = d.get("source_file")
+    if src is None or d.get("attn_source_sha256_16") != kernel_source_hash(src):
         return None
     return d.get("bytes_per_launch")
 
