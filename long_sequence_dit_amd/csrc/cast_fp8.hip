@@ -42,28 +42,36 @@ __global__ void amax_clear_kernel(float* amax, int n) {
   if (i < n) amax[i] = 0.0f;
 }
 
-// One wave per (t, b, h, chunk of 64 tokens); each pass covers 4 tokens x 256 B
-// (16 lanes per token row of D = 128 channels).
-__global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_chunks) {
+// One wave per (t, b, h, run of 256 tokens); a pass covers 4 tokens x 256 B
+// (16 lanes per token row of D = 128 channels).  The loads of 8 passes are
+// issued before any arithmetic; rows past S re-read row S - 1 (harmless for a
+// maximum), so the loop has no branches.
+constexpr int kAmaxRun = 256;
+
+__global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs) {
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t n_waves = (int64_t)3 * a.B * a.H * n_chunks;
+  const int64_t n_waves = (int64_t)3 * a.B * a.H * n_runs;
   if (w >= n_waves) return;
-  const int chunk = (int)(w % n_chunks);
-  const int64_t tbh = w / n_chunks;
+  const int run = (int)(w % n_runs);
+  const int64_t tbh = w / n_runs;
   const int h = (int)(tbh % a.H);
   const int b = (int)((tbh / a.H) % a.B);
   const int t = (int)(tbh / ((int64_t)a.H * a.B));
-  const uint16_t* base = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t];
-  const int vec = lane & 15;   // 16-byte vector within the 256-byte row
+  const uint16_t* base = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t] + 8 * (lane & 15);
+  const int s0 = run * kAmaxRun + (lane >> 4);
   float m = 0.0f;
-  for (int i = lane >> 4; i < kChunk; i += 4) {
-    const int s = chunk * kChunk + i;
-    if (s < a.S) {
-      const u32x4 x = *(const u32x4*)(base + (int64_t)s * a.src_ss[t] + 8 * vec);
+  for (int i0 = 0; i0 < kAmaxRun; i0 += 32) {
+    u32x4 x[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[e])), fabsf(bf16_hi(x[e]))));
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + i0 + 4 * u, a.S - 1);
+      x[u] = *(const u32x4*)(base + (int64_t)s * a.src_ss[t]);
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[u][e])), fabsf(bf16_hi(x[u][e]))));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -151,11 +159,12 @@ hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(amax_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.amax, n);
   if (a.S == 0) return hipGetLastError();
   const int n_chunks = (a.S + kChunk - 1) / kChunk;
-  const int64_t amax_waves = (int64_t)3 * a.B * a.H * n_chunks;
+  const int n_runs = (a.S + kAmaxRun - 1) / kAmaxRun;
+  const int64_t amax_waves = (int64_t)3 * a.B * a.H * n_runs;
   const int64_t qk_waves = (int64_t)2 * a.B * a.H * n_chunks;
   const int64_t vt_blocks = (int64_t)a.B * a.H * n_chunks;
   if ((amax_waves + 3) / 4 > 0x7fffffff || vt_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)((amax_waves + 3) / 4)), dim3(256), 0, stream, a, n_chunks);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)((amax_waves + 3) / 4)), dim3(256), 0, stream, a, n_runs);
   hipLaunchKernelGGL(quant_qk_kernel, dim3((unsigned)((qk_waves + 3) / 4)), dim3(256), 0, stream, a, n_chunks);
   hipLaunchKernelGGL(quant_vt_kernel, dim3((unsigned)vt_blocks), dim3(256), 0, stream, a, n_chunks);
   return hipGetLastError();
