@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lsd_internal.h"
 
 namespace lsd {
@@ -200,39 +202,41 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   const int vp_chunk = v_loader ? 2 * (tid >> 6) + (tid & 1) : 0;
   const uint32_t v_off0 = (uint32_t)(2 * vp_pair * a.v_ss + 8 * vp_chunk) * 2u;
   const uint32_t v_off1 = v_off0 + (uint32_t)a.v_ss * 2u;
-  u32x4 kst[C::kLoadsPerThread], vst[2];
+  u32x4 kst[2][C::kLoadsPerThread], vst[2][2];  // [tile parity]
   auto tile_bytes = [&](int t, int64_t ss) -> int {
     const int64_t rows = (int64_t)skv - (int64_t)t * kBlockN;
     const int64_t any = -(int64_t)(rows > 0);  // all ones if a row is left
     const int64_t n = ((min(rows, (int64_t)kBlockN) - 1) * ss * 2 + 2 * D) & any;
     return (int)n;
   };
-  auto load_k = [&](int t) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto load_k = [&](int t, auto par) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (int64_t)t * kBlockN * a.k_ss), (short)0, tile_bytes(t, a.k_ss), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < C::kLoadsPerThread; ++u) kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off[u], 0, 0);
+    for (int u = 0; u < C::kLoadsPerThread; ++u) kst[par()][u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off[u], 0, 0);
   };
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t, auto par) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + (int64_t)t * kBlockN * a.v_ss), (short)0, tile_bytes(t, a.v_ss), 0x00020000);
-    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
-    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
+    vst[par()][0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
+    vst[par()][1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
   };
-  auto store_k = [&](int t) {
+  auto store_k = [&](int t, auto par) {
 #pragma unroll
     for (int u = 0; u < C::kLoadsPerThread; ++u)
-      *(u32x4*)(Ks + (t & 1) * C::kLdsK + k_row[u] * C::kRowK + 8 * k_ch[u]) = kst[u];
+      *(u32x4*)(Ks + (t & 1) * C::kLdsK + k_row[u] * C::kRowK + 8 * k_ch[u]) = kst[par()][u];
   };
   // V^T[d][vt_pos(j)]: for each of the 8 channels d of the chunk, one dword
   // holding (V[2p][d], V[2p+1][d]); vt_pos keeps key pairs adjacent.
   const int vt_col = vt_pos(2 * vp_pair);
-  auto store_v = [&](int t) {
+  auto store_v = [&](int t, auto par) {
     uint16_t* dst = Vs + (t & 1) * C::kLdsV + (8 * vp_chunk) * C::kRowVT + vt_col;
     if (C::kChunksPerRow == 16 || v_loader) {  // every thread carries V when D = 128
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = __builtin_amdgcn_perm(vst[1][e >> 1], vst[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        const uint32_t w = __builtin_amdgcn_perm(vst[par()][1][e >> 1], vst[par()][0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         *(uint32_t*)(dst + e * C::kRowVT) = w;
       }
     }
@@ -324,7 +328,9 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     const int kb = j / C::kDSteps, s2 = j % C::kDSteps;
     return Ks + ((t + 1) & 1) * C::kLdsK + (32 * kb + l32) * C::kRowK + 8 * hh + 16 * s2;
   };
-  auto mfma_phase = [&](int t) {
+  auto mfma_phase = [&](int t, auto par) {
+    using P = decltype(par);
+    using Q = std::integral_constant<int, 1 - P::value>;
     u32x4 fr[kDist];
 #pragma unroll
     for (int i = 0; i < kDist; ++i) fr[i] = *(const u32x4*)frag_ptr(i, t);
@@ -344,10 +350,13 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
         const f32x16 acc_in = (s2 == 0) ? (f32x16){} : sacc[kb];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur), qreg[s2], acc_in, 0, 0, 0);
       }
-      if (i == 2) store_k(t + 2);
-      if (i == 3) store_v(t + 1);
-      if (i == 6) load_k(t + 3);
-      if (i == 8) load_v(t + 2);
+      // staging registers per tile parity: K(t+2) and V(t+1) leave for LDS,
+      // and their slots take the loads of K(t+4) and V(t+3), two iterations
+      // ahead of their stores
+      if (i == 2) store_k(t + 2, P{});
+      if (i == 3) store_v(t + 1, Q{});
+      if (i == 6) load_k(t + 4, P{});
+      if (i == 8) load_v(t + 3, Q{});
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -366,15 +375,17 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // the last tile the loads have an empty range (they return zero) and the LDS
   // writes fill buffers whose contents are never used.
   const int group = wave >> 2;
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  load_k(1);
-  store_k(1);
+  load_k(0, I0{});
+  load_v(0, I0{});
+  store_k(0, I0{});
+  store_v(0, I0{});
+  load_k(1, I1{});
+  store_k(1, I1{});
   __syncthreads();
-  load_k(2);
-  load_v(1);
+  load_k(2, I0{});
+  load_k(3, I1{});
+  load_v(1, I1{});
+  load_v(2, I0{});
 
   {  // QK(0)
     const uint16_t* kp = Ks + l32 * C::kRowK + 8 * hh;
@@ -388,14 +399,18 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     }
   }
   if (group == 1) lds_barrier();
-  for (int t = 0; t < n_tiles; ++t) {
+  auto iteration = [&](int t, auto par) {
     if ((t + 1) * kBlockN > skv) mask_tail(t);
     softmax();
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase(t);
+    mfma_phase(t, par);
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {  // unrolled by two: tile parity is a constant
+    iteration(t, I0{});
+    if (t + 1 < n_tiles) iteration(t + 1, I1{});
   }
   if (group == 0) lds_barrier();
 
