@@ -10,7 +10,8 @@
 // HBM-bound stream.  One workgroup covers 64 consecutive sequence positions of
 // one (b, h): the 64 x n LSE values are read coalesced and turned into
 // normalised weights in LDS, then each 16-lane group streams one 256-byte
-// (D = 128) output row, reading the n partial rows it combines.
+// (D = 128) output row, reading the n partial rows it combines (non-temporal
+// loads and stores: each byte is touched once).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,8 +79,8 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a,
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < a.n; ++i) {
       const float w = w_s[i][row];
-      const u32x4 v = *(const u32x4*)(a.o_in[i] + (int64_t)b * a.in_sb[i] + (int64_t)s * a.in_ss[i] +
-                                       (int64_t)h * a.in_sh[i] + 8 * c);
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.o_in[i] + (int64_t)b * a.in_sb[i] +
+                                                                 (int64_t)s * a.in_ss[i] + (int64_t)h * a.in_sh[i] + 8 * c));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[2 * e] += w * __uint_as_float(v[e] << 16);
@@ -88,7 +89,8 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a,
     }
     const u32x4 out = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
                        pack_bf16(acc[6], acc[7])};
-    *(u32x4*)(a.o_out + (int64_t)b * a.out_sb + (int64_t)s * a.out_ss + (int64_t)h * a.out_sh + 8 * c) = out;
+    __builtin_nontemporal_store(out, (u32x4*)(a.o_out + (int64_t)b * a.out_sb + (int64_t)s * a.out_ss +
+                                              (int64_t)h * a.out_sh + 8 * c));
   }
 }
 

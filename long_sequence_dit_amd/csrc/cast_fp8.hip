@@ -13,7 +13,7 @@
 //
 // Three launches on the caller's stream: clear amax, reduce it (integer max
 // on the float bits of non-negative values: order-independent, so the result
-// is deterministic), then quantise.
+// is deterministic), then quantise.  Bulk loads and stores are non-temporal.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int s = min(s0 + i0 + 4 * u, a.S - 1);
-      x[u] = *(const u32x4*)(base + (int64_t)s * a.src_ss[t]);
+      x[u] = __builtin_nontemporal_load((const u32x4*)(base + (int64_t)s * a.src_ss[t]));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -99,11 +99,11 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
   for (int i = lane >> 4; i < kChunk; i += 4) {
     const int s = chunk * kChunk + i;
     if (s < a.S) {
-      const u32x4 x = *(const u32x4*)(src + (int64_t)s * a.src_ss[t] + 8 * vec);
+      const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[t] + 8 * vec));
       u32x2 c;
       c[0] = pack4_fp8(bf16_lo(x[0]) * inv, bf16_hi(x[0]) * inv, bf16_lo(x[1]) * inv, bf16_hi(x[1]) * inv);
       c[1] = pack4_fp8(bf16_lo(x[2]) * inv, bf16_hi(x[2]) * inv, bf16_lo(x[3]) * inv, bf16_hi(x[3]) * inv);
-      *(u32x2*)(dst + (int64_t)s * a.dst_ss[t] + 8 * vec) = c;
+      __builtin_nontemporal_store(c, (u32x2*)(dst + (int64_t)s * a.dst_ss[t] + 8 * vec));
     }
   }
 }
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   for (int i = 0; i < 4; ++i) {
     const int s = s0 + 4 * g + i;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (s < a.S) x = *(const u32x4*)(src + (int64_t)s * a.src_ss[2] + 8 * c);
+    if (s < a.S) x = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[2] + 8 * c));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[i][2 * e] = bf16_lo(x[e]) * inv;
@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   for (int p = tid; p < 128 * 4; p += 256) {
     const int d = p >> 2, q = p & 3;
     const u32x4 val = *(const u32x4*)(tile + d * 80 + 16 * q);   // tokens >= S were loaded as 0
-    *(u32x4*)(dst + (int64_t)d * a.dst_sd_v + s0 + 16 * q) = val;
+    __builtin_nontemporal_store(val, (u32x4*)(dst + (int64_t)d * a.dst_sd_v + s0 + 16 * q));
   }
 }
 
