@@ -62,7 +62,7 @@ typedef enum lsd_status {
 typedef struct lsd_view4 {
   void* data;        /* device pointer to element [0,0,0,0] */
   int64_t shape[4];  /* (B, S, H, D) */
-  int64_t stride[4]; /* element strides; stride[3] == 1 */
+  int64_t stride[4]; /* element strides; stride[3] == 1 unless stated */
 } lsd_view4;
 
 /* LSD_ABI_VERSION of the built library. */
@@ -90,9 +90,22 @@ const char* lsd_last_error(void);
  * S_q and S_kv may differ (a query block against a key/value block).
  * S_kv == 0 gives O = 0 and LSE = -inf.  Zero-sized B, S_q or H is a no-op.
  * softmax_scale <= 0 (or NaN) selects 1/sqrt(D); +inf is rejected.
- * D must be 64 or 128, and the sequence strides of k and v must be below
- * 2^24 elements (LSD_EUNSUPPORTED otherwise).  The device must be gfx950
- * (LSD_EUNSUPPORTED otherwise).
+ *
+ * v may be given in either layout, told apart by its strides:
+ *   natural          stride[3] == 1 (each token's channels contiguous);
+ *   token-contiguous stride[1] == 1 and stride[3] = row pitch: each
+ *                    channel's S_kv keys form one row (storage [B, H, D, pitch]
+ *                    in the usual case).  The pitch must be at least S_kv, a
+ *                    multiple of 8 and below 2^23; stride[0] and stride[2]
+ *                    multiples of 8.  Only keys below S_kv (below kv_lens[b]
+ *                    in the masked calls) are read, so row padding may hold
+ *                    anything.  This is the layout the kernel stages straight
+ *                    into LDS, the faster of the two; results are identical.
+ * All other strides (and every stride but the unit one of v) must be multiples
+ * of 8 elements and the data pointers 16-byte aligned (LSD_EINVAL otherwise).
+ * D must be 64 or 128, and the sequence stride of k (and of a natural v) must
+ * be below 2^24 elements (LSD_EUNSUPPORTED otherwise).  The device must be
+ * gfx950 (LSD_EUNSUPPORTED otherwise).
  */
 lsd_status lsd_attn_fwd(const lsd_view4* q, const lsd_view4* k, const lsd_view4* v,
                         const lsd_view4* o, float* lse, float softmax_scale, void* stream);

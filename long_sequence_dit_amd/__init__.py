@@ -135,7 +135,8 @@ def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_ls
     """O = softmax(scale * Q K^T) V per (batch, head), plus the natural-log LSE.
 
     q: (B, S_q, H, D) bf16, k/v: (B, S_kv, H, D) bf16 (strided views allowed,
-    last dim contiguous).  Returns ``o`` (and ``lse`` [B, H, S_q] float32 when
+    last dim contiguous; v may instead be token-contiguous, see
+    ``v_token_major``).  Returns ``o`` (and ``lse`` [B, H, S_q] float32 when
     ``return_lse``).  ``scale`` defaults to 1/sqrt(D).  ``kv_lens`` (int32 [B]
     on the GPU) is a key-only padding mask: batch entry b attends its first
     kv_lens[b] keys.
@@ -215,6 +216,19 @@ def _view8(t, name):
         v.shape[i] = t.shape[i]
         v.stride[i] = t.stride(i)
     return v
+
+
+def v_token_major(B, S, H, D, device="cuda", pitch=None):
+    """Allocate a bf16 V stored token-contiguous: a (B, S, H, D) view whose
+    storage is [B, H, D, pitch] (each channel's S keys one row; pitch defaults
+    to S rounded up to 8).  Attention stages such a V straight from HBM into
+    LDS, and ``relayout_seq_to_head`` writes V in this layout when given one."""
+    torch = _torch()
+    p = (S + 7) // 8 * 8 if pitch is None else int(pitch)
+    if p < S or p % 8 != 0:
+        raise ValueError(f"v_token_major: pitch {p} must be a multiple of 8 and at least S={S}")
+    vt = torch.empty((B, H, D, p), dtype=torch.bfloat16, device=device)
+    return vt.permute(0, 3, 1, 2)[:, :S]
 
 
 def fp8_buffers(B, S, H, D=128, device="cuda"):

@@ -66,8 +66,10 @@ bool overlaps(const Span& a, const Span& b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Structural checks shared by every bf16 view.
-lsd_status check_view(const char* name, const lsd_view4* v) {
+// Structural checks shared by every bf16 view.  The unit-stride dimension is
+// the head channel (unit_dim 3), or the sequence (unit_dim 1) for a V given
+// token-contiguous; every other stride is a multiple of 16 bytes.
+lsd_status check_view(const char* name, const lsd_view4* v, int unit_dim = 3) {
   if (v == nullptr) return fail(LSD_EINVAL, "%s: null view", name);
   for (int i = 0; i < 4; ++i) {
     if (v->shape[i] < 0) return fail(LSD_EINVAL, "%s: negative shape[%d]", name, i);
@@ -76,12 +78,13 @@ lsd_status check_view(const char* name, const lsd_view4* v) {
   }
   if (view_empty(*v)) return LSD_OK;
   if (v->data == nullptr) return fail(LSD_EINVAL, "%s: null data pointer", name);
-  if (v->stride[3] != 1 && v->shape[3] > 1)
-    return fail(LSD_EINVAL, "%s: stride[3] must be 1 (head channels contiguous)", name);
+  if (v->stride[unit_dim] != 1 && v->shape[unit_dim] > 1)
+    return fail(LSD_EINVAL, "%s: stride[%d] must be 1 (%s contiguous)", name, unit_dim,
+                unit_dim == 3 ? "head channels" : "tokens");
   if ((uintptr_t)v->data % 16 != 0) return fail(LSD_EINVAL, "%s: data pointer not 16-byte aligned", name);
   if (v->shape[3] % 8 != 0) return fail(LSD_EINVAL, "%s: D=%lld is not a multiple of 8", name, (long long)v->shape[3]);
-  for (int i = 0; i < 3; ++i)
-    if (v->shape[i] > 1 && v->stride[i] % 8 != 0)
+  for (int i = 0; i < 4; ++i)
+    if (i != unit_dim && v->shape[i] > 1 && v->stride[i] % 8 != 0)
       return fail(LSD_EINVAL, "%s: stride[%d]=%lld is not a multiple of 8 elements (16 bytes)", name, i,
                   (long long)v->stride[i]);
   // the largest element offset must fit comfortably in 64-bit byte arithmetic
@@ -114,6 +117,26 @@ lsd_status check_view8(const char* name, const lsd_view4* v, int unit_dim) {
   double last = 0;
   for (int i = 0; i < 4; ++i) last += (double)(v->shape[i] - 1) * (double)v->stride[i];
   if (last > 9.0e18) return fail(LSD_EINVAL, "%s: view spans more than 2^62 bytes", name);
+  return LSD_OK;
+}
+
+// Layout of a V view: token-contiguous (V^T rows: stride[1] = 1, channel
+// stride = row pitch) when its channels are not unit-stride.
+bool v_token_major(const lsd_view4* v) {
+  return v != nullptr && v->stride[3] != 1 && v->shape[3] > 1 && v->stride[1] == 1;
+}
+
+// A token-contiguous V's rows hold all S keys, do not overlap, and are
+// addressed with 32-bit byte offsets.
+lsd_status check_vt_rows(const char* name, const lsd_view4* v) {
+  if (view_empty(*v)) return LSD_OK;
+  const int64_t S = v->shape[1], D = v->shape[3];
+  if (D > 1 && v->stride[3] < S)
+    return fail(LSD_EINVAL, "%s: token-contiguous rows: pitch stride[3]=%lld is below S=%lld", name,
+                (long long)v->stride[3], (long long)S);
+  if (v->stride[3] >= (int64_t(1) << 23))
+    return fail(LSD_EUNSUPPORTED, "%s: token-contiguous rows: pitch stride[3]=%lld must be below 2^23", name,
+                (long long)v->stride[3]);
   return LSD_OK;
 }
 
@@ -157,7 +180,9 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   lsd_status s;
   if ((s = check_view("q", q)) != LSD_OK) return s;
   if ((s = check_view("k", k)) != LSD_OK) return s;
-  if ((s = check_view("v", v)) != LSD_OK) return s;
+  const bool v_tok = v_token_major(v);
+  if ((s = check_view("v", v, v_tok ? 1 : 3)) != LSD_OK) return s;
+  if (v_tok && (s = check_vt_rows("v", v)) != LSD_OK) return s;
   if ((!acc || o != nullptr) && (s = check_view("o", o)) != LSD_OK) return s;
   const int64_t B = q->shape[0], S_q = q->shape[1], H = q->shape[2], D = q->shape[3];
   const int64_t S_kv = k->shape[1];
@@ -169,7 +194,7 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   if (o != nullptr && !same_shape(*o, *q)) return fail(LSD_EINVAL, "o shape must equal q shape (B, S_q, H, D)");
   if (D != 64 && D != 128) return fail(LSD_EUNSUPPORTED, "head dim D=%lld unsupported (64 or 128)", (long long)D);
   // a 64-key K/V tile is addressed with 32-bit byte offsets
-  if (k->stride[1] >= (int64_t(1) << 24) || v->stride[1] >= (int64_t(1) << 24))
+  if (k->stride[1] >= (int64_t(1) << 24) || (!v_tok && v->stride[1] >= (int64_t(1) << 24)))
     return fail(LSD_EUNSUPPORTED, "k/v sequence stride (%lld, %lld elements) must be below 2^24",
                 (long long)k->stride[1], (long long)v->stride[1]);
   if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
@@ -214,6 +239,8 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
   a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
   a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
+  a.v_sd = v->stride[3];
+  a.v_tok = v_tok ? 1 : 0;
   if (o != nullptr) { a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2]; }
   a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv; a.D = (int)D;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);

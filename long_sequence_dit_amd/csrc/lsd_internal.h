@@ -24,6 +24,10 @@ struct AttnArgs {
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
+  // v_tok = 1: V is token-contiguous (stride of the sequence dim is 1), each
+  // channel's keys a row of pitch v_sd elements (V^T per head); 0: natural.
+  int64_t v_sd;
+  int v_tok;
   int64_t o_sb, o_ss, o_sh;
   int B, H, S_q, S_kv, D;
   float scale_log2;  // softmax scale * log2(e)

@@ -299,6 +299,38 @@ def test_attn_fwd_rejects_huge_kv_stride():
     assert r == LSD_EUNSUPPORTED and "2^24" in msg
 
 
+def vt_view(addr, B, S, H, D, pitch):
+    # token-contiguous V: storage [B, H, D, pitch]
+    return view(addr, (B, S, H, D), [H * D * pitch, 1, D * pitch, pitch])
+
+
+def test_attn_fwd_token_major_v_validation():
+    q, k, _, o = good4(S_kv=300)
+    B, S_kv, H, D = 1, 300, 2, 64
+    # accepted layout: validation passes, so the call reaches the device check
+    # (no GPU here) instead of failing on the view
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 304), o)
+    assert "v:" not in msg and "pitch" not in msg
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 296), o)
+    assert r == LSD_EINVAL and "below S=300" in msg
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 308), o)
+    assert r == LSD_EINVAL and "stride[3]" in msg and "multiple of 8" in msg
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 1 << 23), o)
+    assert r == LSD_EUNSUPPORTED and "2^23" in msg
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB + 2, B, S_kv, H, D, 304), o)
+    assert r == LSD_EINVAL and "16-byte aligned" in msg
+    # neither channels nor tokens unit-stride
+    r, msg = attn(q, k, view(BASE + 2 * GB, (B, S_kv, H, D), [S_kv * H * D * 2, 2, S_kv * D * 2, 8]), o)
+    assert r == LSD_EINVAL and "stride[3] must be 1" in msg
+    # a token-contiguous v may have a huge batch stride (the 2^24 limit is on k and natural v)
+    vt = view(BASE + 2 * GB, (B, S_kv, H, D), [1 << 30, 1, D * 304, 304])
+    r, msg = attn(q, k, vt, o)
+    assert "2^24" not in msg and "v:" not in msg
+    # overlap with an output is still caught
+    r, msg = attn(q, k, vt_view(BASE + 3 * GB, B, S_kv, H, D, 304), o)
+    assert r == LSD_EINVAL and "overlaps" in msg
+
+
 def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
