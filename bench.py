@@ -87,6 +87,15 @@ def to_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def token_major(v):
+    """The same V values stored token-contiguous (each channel's keys one row)."""
+    import long_sequence_dit_amd as lsd
+    B, S, H, D = v.shape
+    vt = lsd.v_token_major(B, S, H, D)
+    vt.copy_(v)
+    return vt
+
+
 class Pipeline:
     """Device tensors and the launch sequence of one step."""
 
@@ -114,11 +123,13 @@ class Pipeline:
             self.src = [[self.fused[:, p * S_loc:(p + 1) * S_loc, t] for p in range(P)] for t in range(3)]
             hl = H // P
             self.qkv = [torch.empty((B, S, hl, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+            if not w.get("fp8"):  # the relayout writes V token-contiguous, the layout attention stages directly
+                self.qkv[2] = lsd.v_token_major(B, S, hl, D)
             self.Hq = hl
         elif name in ("ring", "ring_stream"):
             q, k, v = synth.qkv(B, S, 3 * S, H, D, seed=w["seed"])
             self.host.update(q=q, k=k, v=v)
-            self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
+            self.qkv = [to_dev(q), to_dev(k), token_major(to_dev(v))]
             self.Hq = H
         elif name == "ltx2_varlen":
             q, k, v = synth.qkv(B, S, S, H, D, seed=w["seed"])
@@ -126,12 +137,12 @@ class Pipeline:
                 k[b, n:] = 0x7FC1                               # padding: any read would poison O
                 v[b, n:] = 0x7FC1
             self.host.update(q=q, k=k, v=v)
-            self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
+            self.qkv = [to_dev(q), to_dev(k), token_major(to_dev(v))]
             self.Hq = H
         else:  # cosmos
             q, k, v, _ = synth.cosmos_qkv(seed=w["seed"], S=S, H=H, D=D)
             self.host.update(q=q, k=k, v=v)
-            self.qkv = [to_dev(q), to_dev(k), to_dev(v)]
+            self.qkv = [to_dev(q), to_dev(k), token_major(to_dev(v))]
             self.Hq = H
         Hq = self.Hq
         self.S_q = self.qkv[0].shape[1]
@@ -455,6 +466,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["desc"], "B": w["B"], "S_q": pipe.S_q, "S_kv": pipe.S_kv, "H": pipe.Hq,
                    "D": w["D"], "kv_blocks": w["kv_blocks"], "fused_merge": pipe.stream,
+                   "v_layout": "token-contiguous" if pipe.qkv[2].stride(1) == 1 else "natural",
                    "flop_per_step": pipe.flops},
         "roofline": {"bound": "mfma", "achieved": round(flops_per_launch / (attn_ms * 1e-3) / 1e12, 1),
                      "peak": peak, "unit": "TFLOP/s",

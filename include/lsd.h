@@ -260,6 +260,12 @@ lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_
  *
  *   dst[t][b, p*S_loc + s, j, :] = src[t*P + p][b, s, rank*(H/P) + j, :]
  *
+ * A destination may instead be token-contiguous (stride[1] == 1, stride[3] =
+ * row pitch, as lsd_attn_fwd accepts V): each channel's P*S_loc tokens are
+ * then written as one row, which lets attention stage V straight into LDS.
+ * Its pitch must be at least P*S_loc, a multiple of 8 and below 2^23, rows and
+ * heads may not overlap (stride[2] >= D*stride[3], stride[0] >= (H/P)*stride[2])
+ * and D must be a multiple of 64; row padding is never written.
  * A pure 16-bit copy: every bit pattern (NaN payloads, -0) is preserved.
  * 1 <= n_tensors <= 3, 1 <= P <= 16, 0 <= rank < P, H % P == 0 (LSD_EINVAL
  * otherwise).  Destinations may not overlap any source or each other.

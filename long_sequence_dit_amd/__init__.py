@@ -284,7 +284,8 @@ def relayout_seq_to_head(src: Sequence[Sequence], P: int, rank: int, dst: Option
 
     src: one list per tensor (1 to 3 of them, e.g. Q, K, V), each holding the P
     sequence shards (B, S_loc, H, D).  Returns one (B, P*S_loc, H/P, D) tensor
-    per source tensor.
+    per source tensor.  A destination given token-contiguous (``v_token_major``)
+    is written in that layout.
     """
     torch = _torch()
     nt = len(src)

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsd.so")
 
-SOURCES = ["api.cpp", "attn_fwd.hip", "attn_merge.hip", "relayout.hip", "cast_fp8.hip", "attn_fp8.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_fwd_vt.hip", "attn_merge.hip", "relayout.hip", "cast_fp8.hip", "attn_fp8.hip"]
 
 ARCH = "gfx950"
 # Packed-FP32 instructions are disabled for all device code: hipcc would

@@ -467,13 +467,27 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
   }
   if ((int64_t)P * S_loc > 0x7fffffff) return fail(LSD_EINVAL, "P*S_loc exceeds 2^31-1");
   const int64_t want1 = inverse ? S_loc : P * S_loc, want2 = inverse ? P * H_loc : H_loc;
+  bool tok[lsd::kMaxRelayoutTensors] = {};
   for (int t = 0; t < n_tensors; ++t) {
     std::snprintf(name, sizeof name, "dst[%d]", t);
-    if ((s = check_view(name, &dst[t])) != LSD_OK) return s;
+    tok[t] = v_token_major(&dst[t]);
+    if (tok[t] && inverse)
+      return fail(LSD_EINVAL, "%s: the inverse relayout writes sequence shards with channels contiguous", name);
+    if ((s = check_view(name, &dst[t], tok[t] ? 1 : 3)) != LSD_OK) return s;
     const lsd_view4& d = dst[t];
     if (d.shape[0] != B || d.shape[1] != want1 || d.shape[2] != want2 || d.shape[3] != D)
       return fail(LSD_EINVAL, "dst[%d] shape must be (B=%lld, %lld, %lld, D=%lld)", t, (long long)B,
                   (long long)want1, (long long)want2, (long long)D);
+    if (tok[t]) {
+      if ((s = check_vt_rows(name, &d)) != LSD_OK) return s;
+      if (D % 64 != 0)
+        return fail(LSD_EUNSUPPORTED, "%s: token-contiguous destination needs D a multiple of 64 (D=%lld)", name,
+                    (long long)D);
+      // rows of one head, heads of one batch entry: disjoint
+      if ((H_loc > 1 && d.stride[2] < D * d.stride[3]) || (B > 1 && d.stride[0] < H_loc * d.stride[2]))
+        return fail(LSD_EINVAL, "%s: token-contiguous destination rows overlap (need stride[2] >= D*stride[3] "
+                                "and stride[0] >= H*stride[2])", name);
+    }
   }
   if (B * S_loc * H_loc * D == 0) return ok();
   for (int t = 0; t < n_tensors; ++t) {
@@ -484,32 +498,46 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
       if (overlaps(sd, span_of(dst[u], 2))) return fail(LSD_EINVAL, "dst[%d] overlaps dst[%d]", t, u);
   }
 
-  lsd::RelayoutArgs a;
+  // Tensors with channel-contiguous destinations go to the run-copy kernel,
+  // token-contiguous ones to the transposing kernel (one launch each).
+  lsd::RelayoutArgs a, at;
   std::memset(&a, 0, sizeof a);
+  std::memset(&at, 0, sizeof at);
   bool contiguous_heads = true;
   for (int t = 0; t < n_tensors; ++t) {
+    lsd::RelayoutArgs& r = tok[t] ? at : a;
+    const int u = r.n_tensors++;
     for (int p = 0; p < P; ++p) {
       const lsd_view4& v = src[t * P + p];
-      a.src[t][p] = (const uint16_t*)v.data;
-      a.src_sb[t][p] = v.stride[0];
-      a.src_ss[t][p] = v.stride[1];
-      a.src_sh[t][p] = v.stride[2];
-      if (H_loc > 1 && v.stride[2] != D) contiguous_heads = false;
+      r.src[u][p] = (const uint16_t*)v.data;
+      r.src_sb[u][p] = v.stride[0];
+      r.src_ss[u][p] = v.stride[1];
+      r.src_sh[u][p] = v.stride[2];
+      if (!tok[t] && H_loc > 1 && v.stride[2] != D) contiguous_heads = false;
     }
-    a.dst[t] = (uint16_t*)dst[t].data;
-    a.dst_sb[t] = dst[t].stride[0];
-    a.dst_ss[t] = dst[t].stride[1];
-    a.dst_sh[t] = dst[t].stride[2];
-    if (H_loc > 1 && dst[t].stride[2] != D) contiguous_heads = false;
+    r.dst[u] = (uint16_t*)dst[t].data;
+    r.dst_sb[u] = dst[t].stride[0];
+    r.dst_ss[u] = dst[t].stride[1];
+    r.dst_sh[u] = dst[t].stride[2];
+    r.dst_sd[u] = dst[t].stride[3];
+    if (!tok[t] && H_loc > 1 && dst[t].stride[2] != D) contiguous_heads = false;
   }
-  a.n_tensors = n_tensors; a.P = P; a.rank = rank; a.B = (int)B; a.S_loc = (int)S_loc;
-  a.H_loc = (int)H_loc; a.D = (int)D;
+  for (lsd::RelayoutArgs* r : {&a, &at}) {
+    r->P = P; r->rank = rank; r->B = (int)B; r->S_loc = (int)S_loc;
+    r->H_loc = (int)H_loc; r->D = (int)D;
+    r->inverse = inverse ? 1 : 0;
+  }
   a.heads_per_run = contiguous_heads ? (int)H_loc : 1;
-  a.inverse = inverse ? 1 : 0;
+  at.heads_per_run = 1;
   if (lsd::relayout_runs(a) > 0x7fffffff)
     return fail(LSD_EUNSUPPORTED, "%s: %lld copy runs exceed 2^31-1", fn, (long long)lsd::relayout_runs(a));
+  const int64_t tok_units = (int64_t)at.n_tensors * B * H_loc * ((P * S_loc + 63) / 64) * (D / 64);
+  if (tok_units > 0x7fffffff)
+    return fail(LSD_EUNSUPPORTED, "%s: %lld token-contiguous tiles exceed 2^31-1", fn, (long long)tok_units);
   if ((s = check_device()) != LSD_OK) return s;
-  return launched(lsd::launch_relayout(a, (hipStream_t)stream), fn);
+  if (a.n_tensors > 0 && (s = launched(lsd::launch_relayout(a, (hipStream_t)stream), fn)) != LSD_OK) return s;
+  if (at.n_tensors > 0) return launched(lsd::launch_relayout_tok(at, (hipStream_t)stream), fn);
+  return ok();
 }
 
 }  // namespace

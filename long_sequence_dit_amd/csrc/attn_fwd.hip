@@ -1,4 +1,5 @@
-// Dense bidirectional attention forward with log-sum-exp, for gfx950.
+// Dense bidirectional attention forward with log-sum-exp, for gfx950: the
+// kernel for V in the natural [B, S, H, D] layout.
 //
 // Computes, per (batch b, head h, query i):
 //   LSE_i = ln sum_j exp(scale * q_i . k_j),   O_i = sum_j exp(scale q_i.k_j - LSE_i) v_j
@@ -14,15 +15,13 @@
 // * Scores are computed transposed, S^T = K Q^T (A = K tile from LDS), so a
 //   lane holds one query row and 16 keys of every 32-key block: the row max and
 //   row sum are in-lane, with one permlane32 swap to combine the two lane halves.
-// * K rows are stored in LDS with bits 2 and 3 of the key index swapped, which
-//   makes accumulator register r of lane half hh score key 16(r/8) + 8hh + r%8:
-//   rounded to bf16, the same registers are directly the B operand (P^T) of the
-//   PV product O^T = V^T P^T, and the matching A operand is a plain 16-byte
-//   read of a V^T row in natural key order.
-// * K tiles reach LDS with direct global->LDS buffer loads (no VGPR staging).
-//   V arrives either token-contiguous (V^T rows in HBM, also loaded directly)
-//   or in the natural [B, S, H, D] layout (transposed in registers on its way
-//   into LDS).  64-key tiles rotate through four LDS stage buffers.
+// * The same accumulator registers, rounded to bf16, are directly the B operand
+//   (P^T) of the PV product O^T = V^T P^T; the key order inside the 16-wide
+//   reduction is permuted to match the accumulator layout.
+// * V is transposed in registers on its way into LDS (key pairs packed with
+//   v_perm), so each PV A operand is one 16-byte LDS read; K is stored
+//   row-major.  K/V tiles of 64 keys are double-buffered in LDS and their
+//   global loads are issued one iteration ahead.
 // * Ping-pong: the two waves that share a SIMD run half an iteration apart, so
 //   one streams MFMAs while the other does the softmax arithmetic.
 // * The row max is tracked lazily: O and l are rescaled only when a row's max
@@ -35,107 +34,48 @@
 
 #include <type_traits>
 
+#include "attn_common.h"
 #include "lsd_internal.h"
 
 namespace lsd {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace attn;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;       // query rows per workgroup
-constexpr int kBlockN = 64;                // keys per LDS tile
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
-constexpr int kStages = 4;                 // LDS stage buffers
-
-// kVT: V is given token-contiguous (V^T rows) and loaded straight into LDS.
-template <int D, bool kVT>
+template <int D>
 struct Cfg {
+  // K row pitch (elements): 16-byte skew per row, so 16 lanes reading one
+  // 16-byte column of 16 consecutive rows hit distinct banks.
+  static constexpr int kRowK = D + 8;
+  // V is stored transposed, V^T[d][vt_pos(j)], 64 keys per row in the order the
+  // PV MFMA consumes them; a pitch of 72 elements (36 dwords) makes both the
+  // transposing 4-byte writes and the 16-byte operand reads conflict-free.
+  static constexpr int kRowVT = 72;
   static constexpr int kDSteps = D / 16;           // QK^T reduction steps
   static constexpr int kDBlocks = D / 32;          // O^T row blocks
-  static constexpr int kCPR = D / 8;               // 16-byte chunks per K row
-  static constexpr int kRowsPerLine = 16 / kCPR;   // K rows per 256 bytes
-  static constexpr int kDma = D / 64;              // direct loads per thread per K (or V^T) tile
-  static constexpr int kTileBytes = kBlockN * D * 2;
-  // V^T rows transposed in registers use a pitch of 72 elements (36 dwords):
-  // both the 4-byte transposing writes and the 16-byte operand reads are then
-  // conflict-free.  Rows loaded directly are 128 bytes, XOR-swizzled instead.
-  static constexpr int kRowVT = 72;
-  static constexpr int kVBytes = kVT ? kTileBytes : D * kRowVT * 2;
-  static constexpr int kVRegion = kStages * kTileBytes;  // V^T buffers start here
-  static constexpr int kLdsBytes = kVRegion + kStages * kVBytes;
+  static constexpr int kChunksPerRow = D / 8;      // 16-byte chunks per row
+  static constexpr int kLoadsPerThread = kBlockN * kChunksPerRow / kThreads;  // K chunks per thread
+  static constexpr int kLdsK = kBlockN * kRowK;    // elements per K buffer
+  static constexpr int kLdsV = D * kRowVT;         // elements per V^T buffer
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from a buffer straight into LDS, lane i's bytes at
-// lds + 16 i (lds must be wave-uniform; lanes out of the buffer's range write
-// zeros).  The builtin exists in the device pass only.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-#endif
-}
-
-// Key held by LDS row rho of a K tile: bits 2 and 3 swapped (an involution).
-__device__ inline int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
-
-__device__ inline uint32_t pack_bf16(float a, float b) {
-  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// IEEE maximum: lowers to v_maximum3_f32 without the NaN-quieting copies that
-// fmaxf needs for MFMA results (NaN inputs are outside the contract anyway).
-__device__ inline float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
-
-__device__ inline float partner_max(float x) {
-  // lanes l and l^32 hold the two halves of one query row
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
-__device__ inline float partner_sum(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+// Position of key j (0..63) inside a V^T row.  The PV MFMA's 16-wide
+// reduction slot e of lane half hh carries key 8*(e/4) + 4*hh + e%4 of its
+// 16-key group (the order in which the S^T accumulator holds the weights), so
+// each lane half's 8 keys are stored contiguously.
+__device__ __host__ constexpr int vt_pos(int j) {
+  return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j & 15) >> 3) + (j & 3);
 }
 
 // kAcc: accumulate mode - this block's result is merged into the running
 // (o_acc, lse_acc) in the epilogue (the Ring step's update, done in place).
-// Output of one query row's 16-byte chunk c when its (b, h) has no keys:
-// O = 0 and LSE = -inf; in accumulate mode the running result is unchanged
-// and O, if requested, is that running result in bf16 (0 where there is none).
-__device__ inline void write_empty(const AttnArgs& a, int b, int s, int h, int c) {
-  const int64_t row = ((int64_t)b * a.S_q + s) * a.H + h;
-  const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + s;
-  u32x4 out = {0u, 0u, 0u, 0u};
-  if (a.o_acc != nullptr) {
-    if (a.o == nullptr) return;
-    if (a.lse_acc[lrow] != -INFINITY) {
-      const f32x4* src = (const f32x4*)(a.o_acc + row * a.D + 8 * c);
-      const f32x4 x0 = src[0], x1 = src[1];
-      out = (u32x4){pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]), pack_bf16(x1[0], x1[1]),
-                    pack_bf16(x1[2], x1[3])};
-    }
-  } else if (a.lse != nullptr && c == 0) {
-    a.lse[lrow] = -INFINITY;
-  }
-  *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = out;
-}
-
-template <int D, bool kAcc, bool kVT>
+template <int D, bool kAcc>
 __global__ void __launch_bounds__(kThreads)
 attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
-  using C = Cfg<D, kVT>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::kLdsBytes / 2];
-  uint8_t* const lds = (uint8_t*)smem;
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::kLdsK + C::kLdsV)];
+  uint16_t* Ks = smem;                 // [2][kBlockN][kRowK]
+  uint16_t* Vs = smem + 2 * C::kLdsK;  // [2][D][kRowVT], V transposed
 
   // ---- XCD-aware tile order: dispatch is round-robin over 8 XCDs; give each
   // XCD a contiguous range of (h, b, q-tile) so its CUs share K/V in L2.  The
@@ -188,121 +128,75 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     }
   }
 
-  // ---- Staging.  Stage buffer s (s % kStages) holds K_{s+1} in the K region
-  // and V_s in the V region: the two tiles G(s) reads.  Every load goes
-  // through a buffer descriptor per tile whose range ends with the last valid
-  // key, so lanes past it read (or write) zeros; tiles past the end get an
-  // empty range.
-  // K: direct loads, 1 KB of LDS per wave instruction.  LDS row rho holds key
-  // swap23(rho); its 16-byte chunks are XOR-swizzled by row so that 16 lanes
-  // reading one chunk of 16 rows hit distinct banks.
-  uint32_t k_voff[C::kDma];
+  // ---- global -> register -> LDS staging, with buffer loads.  Each tile
+  // gets a buffer descriptor (built in scalar registers) whose base is the
+  // tile's first row and whose byte range ends with the last valid row, so a
+  // lane's offset inside the tile is fixed for the whole kernel and rows past
+  // the valid keys read as zero (their scores are masked to -inf, so they get zero
+  // weight).  Tiles past the end get an empty range.
+  int k_row[C::kLoadsPerThread], k_ch[C::kLoadsPerThread];
+  uint32_t k_off[C::kLoadsPerThread];
 #pragma unroll
-  for (int u = 0; u < C::kDma; ++u) {
-    const int g = wave * C::kDma + u;
-    const int rho = g * (64 / C::kCPR) + lane / C::kCPR;
-    const int kc = (lane % C::kCPR) ^ ((rho / C::kRowsPerLine) % C::kCPR);
-    k_voff[u] = (uint32_t)(swap23(rho) * (int)a.k_ss + 8 * kc) * 2u;
+  for (int u = 0; u < C::kLoadsPerThread; ++u) {
+    const int idx = tid + kThreads * u;
+    k_row[u] = idx / C::kChunksPerRow;
+    k_ch[u] = idx % C::kChunksPerRow;
+    k_off[u] = (uint32_t)(k_row[u] * a.k_ss + 8 * k_ch[u]) * 2u;
   }
+  // V: thread -> (key pair, 16-byte d-chunk); each wave covers all 32 pairs of
+  // a tile for two chunks, which keeps the transposing writes conflict-free.
+  // For D = 64 only waves 0-3 carry V.
+  const int vp_pair = (tid & 63) >> 1;
+  const bool v_loader = 2 * (tid >> 6) + (tid & 1) < C::kChunksPerRow;
+  const int vp_chunk = v_loader ? 2 * (tid >> 6) + (tid & 1) : 0;
+  const uint32_t v_off0 = (uint32_t)(2 * vp_pair * a.v_ss + 8 * vp_chunk) * 2u;
+  const uint32_t v_off1 = v_off0 + (uint32_t)a.v_ss * 2u;
+  u32x4 kst[2][C::kLoadsPerThread], vst[2][2];  // [tile parity]
   auto tile_bytes = [&](int t, int64_t ss) -> int {
     const int64_t rows = (int64_t)skv - (int64_t)t * kBlockN;
     const int64_t any = -(int64_t)(rows > 0);  // all ones if a row is left
     const int64_t n = ((min(rows, (int64_t)kBlockN) - 1) * ss * 2 + 2 * D) & any;
     return (int)n;
   };
-  auto dma_k = [&](int t, uint8_t* dst) {  // K tile t -> dst
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto load_k = [&](int t, auto par) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (int64_t)t * kBlockN * a.k_ss), (short)0, tile_bytes(t, a.k_ss), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < C::kDma; ++u) dma16(r, dst + (wave * C::kDma + u) * 1024, k_voff[u]);
+    for (int u = 0; u < C::kLoadsPerThread; ++u) kst[par()][u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off[u], 0, 0);
   };
-  uint8_t* const vregion = lds + C::kVRegion;
-  // V^T given (kVT): direct loads of 128-byte rows (64 keys of one channel),
-  // 16-byte chunks XOR-swizzled by row pair.  A chunk is loaded only when all
-  // 8 of its keys are valid; the one chunk per row that straddles the key
-  // count (when it is not a multiple of 8) is filled in afterwards.
-  uint32_t v_voff[C::kDma];
-  int v_key[C::kDma];
-#pragma unroll
-  for (int u = 0; u < C::kDma; ++u) {
-    const int d = (wave * C::kDma + u) * 8 + lane / 8;
-    const int vc = (lane % 8) ^ ((d >> 1) & 7);
-    v_voff[u] = (uint32_t)(d * (int)a.v_sd + 8 * vc) * 2u;
-    v_key[u] = 8 * vc;
-  }
-  const int vt_range = (int)(((int64_t)(D - 1) * a.v_sd + kBlockN) * 2);
-  auto dma_v = [&](int t, uint8_t* dst) {  // V^T tile t -> dst
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (int64_t)t * kBlockN), (short)0, vt_range, 0x00020000);
-#pragma unroll
-    for (int u = 0; u < C::kDma; ++u) {
-      const uint32_t off = (t * kBlockN + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u;
-      dma16(r, dst + (wave * C::kDma + u) * 1024, off);
-    }
-  };
-  auto fill_straddle = [&](int t) {  // tile t holds key skv - 1 and skv % 8 != 0
-    uint8_t* vb = vregion + (t % kStages) * C::kVBytes;
-#pragma unroll
-    for (int u = 0; u < C::kDma; ++u) {
-      const int k0 = t * kBlockN + v_key[u];
-      if (k0 < skv && k0 + 8 > skv) {
-        const int d = (wave * C::kDma + u) * 8 + lane / 8;
-        const uint16_t* src = vbase + (int64_t)d * a.v_sd + k0;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (k0 + 2 * e < skv) ? src[2 * e] : 0u;
-          const uint32_t hi = (k0 + 2 * e + 1 < skv) ? src[2 * e + 1] : 0u;
-          w[e] = lo | (hi << 16);
-        }
-        *(u32x4*)(vb + (wave * C::kDma + u) * 1024 + 16 * lane) = (u32x4){w[0], w[1], w[2], w[3]};
-      }
-    }
-  };
-  // V natural (!kVT): thread -> (key pair, 16-byte d-chunk); each wave covers
-  // all 32 pairs of a tile for two chunks.  For D = 64 waves 4-7 carry no V
-  // but issue the same loads out of range, so every wave counts the same
-  // loads in flight.  Loads run two iterations ahead of their LDS stores,
-  // double-buffered in registers by tile parity.
-  const int vp_pair = (tid & 63) >> 1;
-  const bool v_loader = 2 * wave + (tid & 1) < C::kCPR;
-  const int vp_chunk = v_loader ? 2 * wave + (tid & 1) : 0;
-  const uint32_t v_off0 = v_loader ? (uint32_t)(2 * vp_pair * (int)a.v_ss + 8 * vp_chunk) * 2u : 0x7ffffff0u;
-  const uint32_t v_off1 = v_loader ? v_off0 + (uint32_t)a.v_ss * 2u : 0x7ffffff0u;
-  u32x4 vst[2][2];  // [tile parity][key of the pair]
   auto load_v = [&](int t, auto par) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + (int64_t)t * kBlockN * a.v_ss), (short)0, tile_bytes(t, a.v_ss), 0x00020000);
     vst[par()][0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
     vst[par()][1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
   };
-  // V^T[d][j]: for each channel d of the chunk one dword (V[2p][d], V[2p+1][d])
-  auto store_v = [&](int buf, auto par) {
-    uint8_t* dst = vregion + buf * C::kVBytes + ((8 * vp_chunk) * C::kRowVT + 2 * vp_pair) * 2;
-    if (v_loader) {
+  auto store_k = [&](int t, auto par) {
+#pragma unroll
+    for (int u = 0; u < C::kLoadsPerThread; ++u)
+      *(u32x4*)(Ks + (t & 1) * C::kLdsK + k_row[u] * C::kRowK + 8 * k_ch[u]) = kst[par()][u];
+  };
+  // V^T[d][vt_pos(j)]: for each of the 8 channels d of the chunk, one dword
+  // holding (V[2p][d], V[2p+1][d]); vt_pos keeps key pairs adjacent.
+  const int vt_col = vt_pos(2 * vp_pair);
+  auto store_v = [&](int t, auto par) {
+    uint16_t* dst = Vs + (t & 1) * C::kLdsV + (8 * vp_chunk) * C::kRowVT + vt_col;
+    if (C::kChunksPerRow == 16 || v_loader) {  // every thread carries V when D = 128
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = __builtin_amdgcn_perm(vst[par()][1][e >> 1], vst[par()][0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-        *(uint32_t*)(dst + e * C::kRowVT * 2) = w;
+        *(uint32_t*)(dst + e * C::kRowVT) = w;
       }
     }
   };
-  // Each lane's fragment addresses (row l32), before stage and row-block
-  // offsets: kfa[s2] for QK step s2, vfa[2 kb + ks] for the PV keys
-  // 32 kb + 16 ks + 8 hh .. + 7.
-  const uint8_t* kfa[C::kDSteps];
-  const uint8_t* vfa[4];
-#pragma unroll
-  for (int s2 = 0; s2 < C::kDSteps; ++s2)
-    kfa[s2] = lds + l32 * (2 * D) + 16 * ((2 * s2 + hh) ^ ((l32 / C::kRowsPerLine) % C::kCPR));
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4)
-    vfa[c4] = kVT ? vregion + l32 * 128 + 16 * ((2 * c4 + hh) ^ ((l32 >> 1) & 7))
-                  : vregion + (l32 * C::kRowVT + 16 * c4 + 8 * hh) * 2;
-  constexpr int kVRowBlock = kVT ? 32 * 128 : 32 * C::kRowVT * 2;  // bytes per 32 V^T rows
-  // Workgroup barrier that orders LDS accesses.  Loads in flight (into VGPRs
-  // or LDS) stay in flight across it: their completion is awaited explicitly.
-  auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // Workgroup barrier that orders LDS only: outstanding global prefetches stay
+  // in flight across it.
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
 
   f32x16 oacc[C::kDBlocks];
 #pragma unroll
@@ -320,7 +214,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = kv0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+        const int j = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (j >= skv) sacc[kb][r] = -INFINITY;
       }
   };
@@ -367,41 +261,33 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // ---- MFMA phase G(t) = PV(t) then QK(t+1), as a fixed list of steps.  Step
   // i issues the LDS read of the operand that step i + kDist consumes, then its
   // own MFMA; sched_barrier fences keep this order, so kDist reads are always
-  // in flight and one wave streams MFMAs back to back.  Loads for later tiles
-  // ride on fixed steps.
+  // in flight and one wave streams MFMAs back to back.  The staging of
+  // K_{t+2} / V_{t+1} into LDS and the global loads of K_{t+3} / V_{t+2} ride
+  // on fixed steps.
   constexpr int kPvSteps = 4 * C::kDBlocks;  // (kb, ks, db)
   constexpr int kQkSteps = 2 * C::kDSteps;   // (kb, s2)
   constexpr int kSteps = kPvSteps + kQkSteps;
   constexpr int kDist = 4;
-  auto frag = [&](int i, auto st) -> u32x4 {
-    constexpr int S = decltype(st)::value;
+  auto frag_ptr = [&](int i, int t) -> const uint16_t* {
     if (i < kPvSteps) {
       const int kb = i / (2 * C::kDBlocks), ks = (i / C::kDBlocks) & 1, db = i % C::kDBlocks;
-      return *(const u32x4*)(vfa[2 * kb + ks] + S * C::kVBytes + db * kVRowBlock);
+      return Vs + (t & 1) * C::kLdsV + (32 * db + l32) * C::kRowVT + 8 * hh + 16 * (2 * kb + ks);
     }
     const int j = i - kPvSteps;
     const int kb = j / C::kDSteps, s2 = j % C::kDSteps;
-    return *(const u32x4*)(kfa[s2] + S * C::kTileBytes + 32 * kb * (2 * D));
+    return Ks + ((t + 1) & 1) * C::kLdsK + (32 * kb + l32) * C::kRowK + 8 * hh + 16 * s2;
   };
-  // Stage t+3 (K_{t+4}, V_{t+3}) goes into the buffer stage t-1 used, free
-  // once both groups have passed G(t-1).  With V natural, V_{t+1} leaves its
-  // registers for LDS and they take the loads of V_{t+3}.  At the end the
-  // wave waits for its own loads of stage t+1, which the next barrier
-  // publishes: in flight may stay stages t+2 and t+3 (and, with V natural,
-  // the V loads of t+1..t+3, issued after stage t+1's K).
-  constexpr int kInFlight = kVT ? 2 * 2 * C::kDma : 2 * C::kDma + 3 * 2;
-  auto mfma_phase = [&](int t, auto st) {
-    constexpr int S = decltype(st)::value;
-    constexpr int kFree = (S + kStages - 1) % kStages;
-    using Par = std::integral_constant<int, (S + 1) & 1>;  // parity of t+1 and t+3
+  auto mfma_phase = [&](int t, auto par) {
+    using P = decltype(par);
+    using Q = std::integral_constant<int, 1 - P::value>;
     u32x4 fr[kDist];
 #pragma unroll
-    for (int i = 0; i < kDist; ++i) fr[i] = frag(i, st);
+    for (int i = 0; i < kDist; ++i) fr[i] = *(const u32x4*)frag_ptr(i, t);
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const u32x4 cur = fr[i % kDist];
-      if (i + kDist < kSteps) fr[i % kDist] = frag(i + kDist, st);
+      if (i + kDist < kSteps) fr[i % kDist] = *(const u32x4*)frag_ptr(i + kDist, t);
       if (i < kPvSteps) {
         const int kb = i / (2 * C::kDBlocks), ks = (i / C::kDBlocks) & 1, db = i % C::kDBlocks;
         const u32x4 pv4 = {pk[kb][4 * ks + 0], pk[kb][4 * ks + 1], pk[kb][4 * ks + 2], pk[kb][4 * ks + 3]};
@@ -413,17 +299,15 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
         const f32x16 acc_in = (s2 == 0) ? (f32x16){} : sacc[kb];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur), qreg[s2], acc_in, 0, 0, 0);
       }
-      if constexpr (kVT) {
-        if (i == 4) dma_k(t + 4, lds + kFree * C::kTileBytes);
-        if (i == 12) dma_v(t + 3, vregion + kFree * C::kVBytes);
-      } else {
-        if (i == 3) store_v((S + 1) % kStages, Par{});
-        if (i == 4) dma_k(t + 4, lds + kFree * C::kTileBytes);
-        if (i == 8) load_v(t + 3, Par{});
-      }
+      // staging registers per tile parity: K(t+2) and V(t+1) leave for LDS,
+      // and their slots take the loads of K(t+4) and V(t+3), two iterations
+      // ahead of their stores
+      if (i == 2) store_k(t + 2, P{});
+      if (i == 3) store_v(t + 1, Q{});
+      if (i == 6) load_k(t + 4, P{});
+      if (i == 8) load_v(t + 3, Q{});
     }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
   };
 
   // ---- Ping-pong schedule.  Waves w and w+4 share a SIMD; group A (waves
@@ -432,70 +316,52 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   // in its VALU phase SM(t):
   //   A: QK(0) SM(0) | G(0) | SM(1) | G(1) | ...
   //   B: QK(0)       | SM(0) | G(0) | SM(1) | ...
-  // G(t) reads stage t during intervals 2t+1 (A) and 2t+2 (B); each group loads
-  // its half of stage t+3 during its G(t) into the buffer of stage t-1, whose
-  // last reader finished in interval 2t, and has its half of stage t+1 landed
-  // by the end of its G(t), before G(t+1) starts for either group.  K_0, read
-  // by QK(0) only, sits in the V buffer of stage 3, first loaded in G(0).
-  // Past the last tile the loads have an empty range (they write zeros) into
-  // buffers whose contents are never used.
+  // LDS: K_t lives in K buffer t%2 and is read during intervals 2t-1 (A) and 2t
+  // (B); V_t in V buffer t%2 during 2t+1 (A) and 2t+2 (B).  Both groups write
+  // their chunks of K_{t+2} and V_{t+1} during their G(t) (intervals 2t+1 and
+  // 2t+2), after every reader of those buffers has passed a barrier, and issue
+  // the global loads of K_{t+3} and V_{t+2}, in flight for one iteration.  Past
+  // the last tile the loads have an empty range (they return zero) and the LDS
+  // writes fill buffers whose contents are never used.
   const int group = wave >> 2;
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  static_assert(kStages == 4, "the main loop is unrolled for four stage buffers");
-  uint8_t* const k0 = vregion + 3 * C::kVBytes;
-  dma_k(0, k0);
-  if constexpr (kVT) {
-#pragma unroll
-    for (int s0 = 0; s0 < kStages - 1; ++s0) {
-      dma_k(s0 + 1, lds + s0 * C::kTileBytes);
-      dma_v(s0, vregion + s0 * C::kVBytes);
-    }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");  // K_0 and stage 0 landed
-    if ((skv & 7) != 0 && n_tiles == 1) fill_straddle(0);
-  } else {
-#pragma unroll
-    for (int s0 = 0; s0 < kStages - 1; ++s0) dma_k(s0 + 1, lds + s0 * C::kTileBytes);
-    load_v(0, I0{});
-    load_v(1, I1{});
-    store_v(0, I0{});  // waits for V_0, and so for every K load issued before it
-    load_v(2, I0{});
-  }
+  load_k(0, I0{});
+  load_v(0, I0{});
+  store_k(0, I0{});
+  store_v(0, I0{});
+  load_k(1, I1{});
+  store_k(1, I1{});
   __syncthreads();
+  load_k(2, I0{});
+  load_k(3, I1{});
+  load_v(1, I1{});
+  load_v(2, I0{});
 
   {  // QK(0)
+    const uint16_t* kp = Ks + l32 * C::kRowK + 8 * hh;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = (f32x16){};
 #pragma unroll
       for (int s2 = 0; s2 < C::kDSteps; ++s2)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, *(const u32x4*)(kfa[s2] - lds + k0 + 32 * kb * (2 * D))), qreg[s2], sacc[kb], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 32 * kb * C::kRowK + 16 * s2)), qreg[s2], sacc[kb], 0, 0, 0);
     }
   }
   if (group == 1) lds_barrier();
-  auto iteration = [&](int t, auto st) {
+  auto iteration = [&](int t, auto par) {
     if ((t + 1) * kBlockN > skv) mask_tail(t);
     softmax();
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
-    mfma_phase(t, st);
+    mfma_phase(t, par);
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (kVT) {
-      if ((skv & 7) != 0 && t + 2 == n_tiles) fill_straddle(t + 1);  // stage t+1 has landed
-    }
     lds_barrier();
   };
-  for (int t = 0; t < n_tiles; t += kStages) {  // unrolled: the stage buffer is a constant
+  for (int t = 0; t < n_tiles; t += 2) {  // unrolled by two: tile parity is a constant
     iteration(t, I0{});
     if (t + 1 < n_tiles) iteration(t + 1, I1{});
-    if (t + 2 < n_tiles) iteration(t + 2, I2{});
-    if (t + 3 < n_tiles) iteration(t + 3, I3{});
   }
   if (group == 0) lds_barrier();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the end still land in LDS
 
   // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l)
   const float l_tot = partner_sum(l_run);
@@ -585,21 +451,22 @@ __global__ void attn_empty_kernel(const AttnArgs a) {
   }
 }
 
-template <int D, bool kVT>
+template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
   const int64_t nblk = (int64_t)n_qtiles * a.H * a.B;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   if (a.o_acc != nullptr)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, true, kVT>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, false, kVT>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+  if (a.S_kv != 0 && a.v_tok) return launch_attn_fwd_vt(a, stream);
   if (a.S_kv == 0) {
     const int64_t n = (int64_t)a.B * a.S_q * a.H * (a.D / 8);
     const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
@@ -607,8 +474,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   switch (a.D) {
-    case 64: return a.v_tok ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
-    case 128: return a.v_tok ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

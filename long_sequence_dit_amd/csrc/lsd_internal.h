@@ -33,6 +33,9 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+// The kernel for a token-contiguous V (v_tok = 1, S_kv > 0); launch_attn_fwd
+// dispatches to it.
+hipError_t launch_attn_fwd_vt(const AttnArgs& a, hipStream_t stream);
 
 constexpr int kMaxMerge = 16;
 
@@ -57,6 +60,9 @@ struct RelayoutArgs {
   int64_t src_sh[kMaxRelayoutTensors][kMaxRelayoutP];
   uint16_t* dst[kMaxRelayoutTensors];
   int64_t dst_sb[kMaxRelayoutTensors], dst_ss[kMaxRelayoutTensors], dst_sh[kMaxRelayoutTensors];
+  // Token-contiguous destinations (launch_relayout_tok): dst_ss is 1 and
+  // dst_sd the row pitch, each channel's tokens one row.
+  int64_t dst_sd[kMaxRelayoutTensors];
   int n_tensors, P, rank, B, S_loc, H_loc, D;
   int heads_per_run;  // H_loc when every head slice is contiguous in src and dst, else 1
   // 0: sequence-major shards -> head-major slice (src[t][p] is shard p of the
@@ -68,6 +74,8 @@ struct RelayoutArgs {
 // Number of copy runs (one per token, tensor and head group) of a relayout.
 int64_t relayout_runs(const RelayoutArgs& a);
 hipError_t launch_relayout(const RelayoutArgs& a, hipStream_t stream);
+// Forward relayout into token-contiguous destinations (inverse = 0 only).
+hipError_t launch_relayout_tok(const RelayoutArgs& a, hipStream_t stream);
 
 // FP8 cast of Q, K, V (D = 128).  Sources are bf16 (B, S, H, D) views; dst[0]
 // and dst[1] are E4M3 (B, S, H, D) views (byte strides, channels contiguous);

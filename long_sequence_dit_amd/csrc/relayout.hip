@@ -102,7 +102,80 @@ __global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a
   }
 }
 
+// Forward relayout into a token-contiguous destination (each channel's
+// P*S_loc tokens one row of pitch dst_sd):
+//   dst[t][b, p*S_loc + s, j, d] = src[t][p][b, s, rank*H_loc + j, d]
+// with the destination stored [b][j][d][token].  One wave moves 64 tokens x
+// 64 channels of one head: lane (c = lane % 8, g = lane / 8) loads 16 bytes
+// (8 channels) of each of the 8 tokens 8g..8g+7, transposes the 8x8 block in
+// registers and stores 16 bytes (8 tokens) of each of its 8 channels, so each
+// load instruction reads 8 whole 128-byte lines (8 tokens, 64 channels) and
+// each store writes 8 (8 channels, 64 tokens).  Tokens past the end are
+// neither read nor written; a row's last partial 8-token group is stored
+// element by element, so row padding is never touched.
+constexpr int kTokWavesPerBlock = 4;
+
+__global__ void __launch_bounds__(64 * kTokWavesPerBlock) relayout_tok_kernel(const RelayoutArgs a, int n_units) {
+  const int lane = threadIdx.x & 63;
+  const int unit = (int)blockIdx.x * kTokWavesPerBlock + (int)(threadIdx.x >> 6);
+  if (unit >= n_units) return;
+  const int S = a.P * a.S_loc;
+  const int n_tblk = (S + 63) / 64;
+  const int n_dh = a.D / 64;
+  // unit = (((t * B + b) * H_loc + j) * n_tblk + tb) * n_dh + dh
+  int rest = unit;
+  const int dh = rest % n_dh; rest /= n_dh;
+  const int tb = rest % n_tblk; rest /= n_tblk;
+  const int j = rest % a.H_loc; rest /= a.H_loc;
+  const int b = rest % a.B;
+  const int t = rest / a.B;
+  const int c = lane & 7, g = lane >> 3;
+  const int tok0 = tb * 64 + 8 * g;
+
+  u32x4 x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int tok = tok0 + k;
+    x[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (tok < S) {
+      const int p = tok / a.S_loc, s = tok - p * a.S_loc;
+      const uint16_t* sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)s * a.src_ss[t][p] +
+                           (int64_t)(a.rank * a.H_loc + j) * a.src_sh[t][p] + 64 * dh + 8 * c;
+      x[k] = __builtin_nontemporal_load((const u32x4*)sp);
+    }
+  }
+  uint16_t* dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)j * a.dst_sh[t] +
+                 (int64_t)(64 * dh + 8 * c) * a.dst_sd[t] + tok0;
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {
+    // tokens 2i, 2i+1 of channel 8c + dd: the 16-bit halves dd%2 of dword dd/2
+    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_perm(x[2 * i + 1][dd >> 1], x[2 * i][dd >> 1], sel);
+    uint16_t* row = dp + (int64_t)dd * a.dst_sd[t];
+    if (tok0 + 8 <= S) {
+      __builtin_nontemporal_store(y, (u32x4*)row);
+    } else if (tok0 < S) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tok0 + e < S) row[e] = (uint16_t)(y[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_relayout_tok(const RelayoutArgs& a, hipStream_t stream) {
+  const int64_t S = (int64_t)a.P * a.S_loc;
+  const int64_t n_units = (int64_t)a.n_tensors * a.B * a.H_loc * ((S + 63) / 64) * (a.D / 64);
+  if (n_units == 0) return hipSuccess;
+  if (n_units > 0x7fffffff || a.D % 64 != 0 || a.inverse) return hipErrorInvalidValue;
+  const int64_t blocks = (n_units + kTokWavesPerBlock - 1) / kTokWavesPerBlock;
+  hipLaunchKernelGGL(relayout_tok_kernel, dim3((unsigned)blocks), dim3(64 * kTokWavesPerBlock), 0, stream, a,
+                     (int)n_units);
+  return hipGetLastError();
+}
 
 int64_t relayout_runs(const RelayoutArgs& a) {
   return (int64_t)a.n_tensors * a.B * a.P * a.S_loc * (a.H_loc / a.heads_per_run);

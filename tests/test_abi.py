@@ -331,6 +331,30 @@ def test_attn_fwd_token_major_v_validation():
     assert r == LSD_EINVAL and "overlaps" in msg
 
 
+def test_relayout_token_major_destination_validation():
+    B, S_loc, H, D, P = 1, 100, 4, 64, 2
+    src = (View4 * (3 * P))(*[view(BASE + i * GB, (B, S_loc, H, D)) for i in range(3 * P)])
+    S, Hl = P * S_loc, H // P
+    def dsts(vt):
+        return (View4 * 3)(view(BASE + 10 * GB, (B, S, Hl, D)), view(BASE + 11 * GB, (B, S, Hl, D)), vt)
+    ok_vt = vt_view(BASE + 12 * GB, B, S, Hl, D, 200)
+    r, msg = relayout(3, P, 0, src, dsts(ok_vt))
+    assert "dst" not in msg
+    r, msg = relayout(3, P, 0, src, dsts(vt_view(BASE + 12 * GB, B, S, Hl, D, 192)))
+    assert r == LSD_EINVAL and "below S=200" in msg
+    r, msg = relayout(3, P, 0, src, dsts(view(BASE + 12 * GB, (B, S, Hl, D), [Hl * D * 200, 1, 104, 200])))
+    assert r == LSD_EINVAL and "overlap" in msg
+    src32 = (View4 * (3 * P))(*[view(BASE + i * GB, (B, S_loc, H, 32)) for i in range(3 * P)])
+    d32 = (View4 * 3)(view(BASE + 10 * GB, (B, S, Hl, 32)), view(BASE + 11 * GB, (B, S, Hl, 32)),
+                      vt_view(BASE + 12 * GB, B, S, Hl, 32, 200))
+    r, msg = relayout(3, P, 0, src32, d32)
+    assert r == LSD_EUNSUPPORTED and "multiple of 64" in msg
+    # the inverse writes channel-contiguous shards only
+    isrc = (View4 * P)(*[view(BASE + i * GB, (B, S, Hl, D)) for i in range(P)])
+    r, msg = relayout_inv(1, P, 0, isrc, (View4 * 1)(vt_view(BASE + 12 * GB, B, S_loc, H, D, 104)))
+    assert r == LSD_EINVAL and "inverse" in msg
+
+
 def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)

@@ -7,7 +7,7 @@ import pytest
 
 import synth
 from oracle import ref
-from gpu_util import note, to_bits, to_dev, torch
+from gpu_util import note, to_bits, to_dev, to_f64, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +125,46 @@ def test_inverse_strided_views_and_guard_bands():
     bb = big.cpu().numpy()
     assert (bb[:, :, 0] == sentinel).all() and (bb[:, :, 2:2 * P * H_loc + 1:2] == sentinel).all()
     assert (bb[:, :, -1] == sentinel).all()
+
+
+@pytest.mark.parametrize("P,S_loc,D", [(1, 37, 128), (4, 25, 128), (2, 64, 64), (4, 1, 64), (1, 300, 128)])
+def test_token_major_destination(P, S_loc, D):
+    note(f"relayout into a token-contiguous V: P={P} S_loc={S_loc} D={D}")
+    t = torch()
+    B, H = 2, 4 * P
+    host = synth.random_bits16((B, P * S_loc, 3, H, D), 77 + P + D)
+    f = to_dev(host)
+    src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    S, Hl = P * S_loc, H // P
+    sentinel = -4242
+    for pitch in ((S + 7) // 8 * 8, (S + 7) // 8 * 8 + 24):
+        store = t.full((B, Hl, D, pitch), sentinel, dtype=t.int16, device="cuda")
+        vt = store.view(t.bfloat16).permute(0, 3, 1, 2)[:, :S]
+        q = t.empty((B, S, Hl, D), dtype=t.bfloat16, device="cuda")
+        k = t.empty_like(q)
+        for r in range(P):
+            lsd.relayout_seq_to_head(src, P, r, dst=[q, k, vt])
+            t.cuda.synchronize()
+            for tt, out in enumerate((q, k, vt)):
+                chunks = [host[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)]
+                assert np.array_equal(to_bits(out), ref.relayout_seq_to_head(chunks, P, r)), (tt, r, pitch)
+            pad = store[..., S:].cpu().numpy()
+            assert (pad == sentinel).all(), "row padding written"
+
+
+def test_token_major_destination_feeds_attention():
+    note("relayout with a token-contiguous V, then attention on it")
+    t = torch()
+    B, S_loc, H, D, P = 1, 200, 4, 128, 2
+    f = to_dev(synth.normal_bf16((B, P * S_loc, 3, H, D), 91, 1))
+    src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    q, k, v = lsd.relayout_seq_to_head(src, P, 1)
+    vt = lsd.v_token_major(B, P * S_loc, H // P, D)
+    q2, k2, vt = lsd.relayout_seq_to_head(src, P, 1, dst=[t.empty_like(q), t.empty_like(k), vt])
+    o1, l1 = lsd.attn_fwd(q, k, v)
+    o2, l2 = lsd.attn_fwd(q2, k2, vt)
+    t.cuda.synchronize()
+    assert np.array_equal(to_bits(q), to_bits(q2)) and np.array_equal(to_bits(vt), to_bits(v))
+    a, b = to_f64(o1), to_f64(o2)
+    assert (np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6).all()
+    assert float((l1 - l2).abs().max()) <= 1e-5

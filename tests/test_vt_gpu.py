@@ -1,9 +1,11 @@
 """Attention with V given token-contiguous (each channel's keys one row, the
-layout staged straight from HBM into LDS), through the C ABI.  Both V layouts
-run the same arithmetic in the same order, so the token-contiguous path must
-match the natural-layout path bit for bit; one case per mode is also checked
-against the oracle.  Row padding and masked keys hold NaN bit patterns, so a
-read of any of them would poison the output."""
+layout staged straight from HBM into LDS), through the C ABI.  That kernel
+assigns keys to the MFMA reduction slots in another order than the kernel for
+the natural layout, so the two agree to within one bf16 rounding step (fp32
+partial sums round differently), and each is checked against the oracle.  The
+token-contiguous kernel itself is bit-reproducible across row pitches and
+padding contents.  Row padding and masked keys hold NaN bit patterns, so a read
+of any of them would poison the output."""
 
 import numpy as np
 import pytest
@@ -52,21 +54,38 @@ CASES = [  # (B, S_q, S_kv, H, D)
 ]
 
 
+def assert_layouts_agree(o1, o2, l1=None, l2=None, what=""):
+    """Outputs of the two kernels: equal up to one bf16 rounding step."""
+    a, b = to_f64(o1), to_f64(o2)
+    assert np.all(np.isfinite(b)), f"{what}: non-finite output"
+    bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6
+    bad = np.abs(a - b) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements differ by more than one bf16 step"
+    if l1 is not None:
+        d = (l1 - l2).abs()
+        d = d[~(l1.isneginf() & l2.isneginf())]
+        assert d.numel() == 0 or float(d.max()) <= 1e-5, f"{what}: LSE differs by {float(d.max()):.2e}"
+
+
 @pytest.mark.parametrize("B,S_q,S_kv,H,D", CASES)
-def test_token_major_v_matches_natural(B, S_q, S_kv, H, D):
+def test_token_major_v(B, S_q, S_kv, H, D):
     note(f"token-major V: B={B} S_q={S_q} S_kv={S_kv} H={H} D={D}")
     t = torch()
     seed = 1000 + S_kv + D
-    q = to_dev(synth.normal_bf16((B, S_q, H, D), seed, 1))
-    k = to_dev(synth.normal_bf16((B, S_kv, H, D), seed + 1, 1))
-    v = to_dev(synth.normal_bf16((B, S_kv, H, D), seed + 2, 1))
+    qh = synth.normal_bf16((B, S_q, H, D), seed, 1)
+    kh = synth.normal_bf16((B, S_kv, H, D), seed + 1, 1)
+    vh = synth.normal_bf16((B, S_kv, H, D), seed + 2, 1)
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
     o1, l1 = lsd.attn_fwd(q, k, v)
+    outs = []
     for pitch in (None, (S_kv + 7) // 8 * 8 + 64):
-        vt = token_major(v, pitch)
-        o2, l2 = lsd.attn_fwd(q, k, vt)
+        o2, l2 = lsd.attn_fwd(q, k, token_major(v, pitch))
         t.cuda.synchronize()
-        assert np.array_equal(to_bits(o1), to_bits(o2)), f"O differs (pitch {pitch})"
-        assert t.equal(l1, l2), f"LSE differs (pitch {pitch})"
+        outs.append((to_bits(o2), l2.clone()))
+        assert_layouts_agree(o1, o2, l1, l2, f"pitch {pitch}")
+    assert np.array_equal(outs[0][0], outs[1][0]) and t.equal(outs[0][1], outs[1][1]), "depends on the pitch"
+    O, L = ref.attention(qh, kh, vh)
+    assert_attention_close(ref.bf16_bits_to_f64(outs[0][0]), O, outs[0][1].cpu().numpy(), L, "token-major")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -89,18 +108,20 @@ def test_token_major_v_masked(D):
     t = torch()
     lens = [300, 1, 63, 64, 65, 129, 0, 257, 7, 250]
     B, S_q, S_kv, H = len(lens), 120, 300, 2
-    q = to_dev(synth.normal_bf16((B, S_q, H, D), 1301, 1))
-    kn = synth.normal_bf16((B, S_kv, H, D), 1302, 1)
+    qh = synth.normal_bf16((B, S_q, H, D), 1301, 1)
+    kh = synth.normal_bf16((B, S_kv, H, D), 1302, 1)
+    vh = synth.normal_bf16((B, S_kv, H, D), 1303, 1)
     for b, n in enumerate(lens):
-        kn[b, n:] = NAN_BITS
-    k = to_dev(kn)
-    v = to_dev(synth.normal_bf16((B, S_kv, H, D), 1303, 1))
+        kh[b, n:] = NAN_BITS
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
     ld = lens_dev(lens)
     o1, l1 = lsd.attn_fwd(q, k, v, kv_lens=ld)
     o2, l2 = lsd.attn_fwd(q, k, token_major(v, lens=lens), kv_lens=ld)
     t.cuda.synchronize()
-    assert np.array_equal(to_bits(o1), to_bits(o2)) and t.equal(l1, l2)
-    assert np.all(np.isfinite(to_f64(o2)))
+    assert_layouts_agree(o1, o2, l1, l2, "masked")
+    O, L = ref.attention(qh, kh, vh, kv_lens=lens)
+    assert_attention_close(to_f64(o2), O, l2.cpu().numpy(), L, "masked token-major")
+    assert (to_f64(o2)[6] == 0).all() and l2[6].isneginf().all()
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -108,9 +129,11 @@ def test_token_major_v_accumulate(D):
     note(f"token-major V in the fused Ring step D={D}")
     t = torch()
     B, S_q, H = 1, 200, 2
-    q = to_dev(synth.normal_bf16((B, S_q, H, D), 1401, 1))
-    blocks = [(to_dev(synth.normal_bf16((B, n, H, D), 1410 + n, 1)),
-               to_dev(synth.normal_bf16((B, n, H, D), 1420 + n, 1))) for n in (150, 77, 300)]
+    qh = synth.normal_bf16((B, S_q, H, D), 1401, 1)
+    q = to_dev(qh)
+    host = [(synth.normal_bf16((B, n, H, D), 1410 + n, 1), synth.normal_bf16((B, n, H, D), 1420 + n, 1))
+            for n in (150, 77, 300)]
+    blocks = [(to_dev(kh), to_dev(vh)) for kh, vh in host]
     res = []
     for tok in (False, True):
         oa = t.zeros((B, S_q, H, D), dtype=t.float32, device="cuda")
@@ -119,6 +142,10 @@ def test_token_major_v_accumulate(D):
         for k, v in blocks:
             lsd.attn_fwd_accumulate(q, k, token_major(v) if tok else v, oa, la, o=o)
         t.cuda.synchronize()
-        res.append((oa.clone(), la.clone(), to_bits(o)))
-    assert t.equal(res[0][0], res[1][0]) and t.equal(res[0][1], res[1][1])
-    assert np.array_equal(res[0][2], res[1][2])
+        res.append((oa.clone(), la.clone(), o.clone()))
+    assert_layouts_agree(res[0][2], res[1][2], res[0][1], res[1][1], "accumulate")
+    assert float((res[0][0] - res[1][0]).abs().max()) <= 1e-5 * max(1.0, float(res[0][0].abs().max()))
+    K = np.concatenate([kh for kh, _ in host], axis=1)
+    V = np.concatenate([vh for _, vh in host], axis=1)
+    O, L = ref.attention(qh, K, V)
+    assert_attention_close(to_f64(res[1][2]), O, res[1][1].cpu().numpy(), L, "accumulate token-major")
