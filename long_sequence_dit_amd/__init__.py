@@ -221,10 +221,12 @@ def _view8(t, name):
 def v_token_major(B, S, H, D, device="cuda", pitch=None):
     """Allocate a bf16 V stored token-contiguous: a (B, S, H, D) view whose
     storage is [B, H, D, pitch] (each channel's S keys one row; pitch defaults
-    to S rounded up to 8).  Attention stages such a V straight from HBM into
-    LDS, and ``relayout_seq_to_head`` writes V in this layout when given one."""
+    to S rounded up to 64, which starts every row on a 128-byte line; any
+    multiple of 8 that is at least S is accepted).  Attention stages such a V
+    straight from HBM into LDS, and ``relayout_seq_to_head`` writes V in this
+    layout when given one."""
     torch = _torch()
-    p = (S + 7) // 8 * 8 if pitch is None else int(pitch)
+    p = (S + 63) // 64 * 64 if pitch is None else int(pitch)
     if p < S or p % 8 != 0:
         raise ValueError(f"v_token_major: pitch {p} must be a multiple of 8 and at least S={S}")
     vt = torch.empty((B, H, D, p), dtype=torch.bfloat16, device=device)
