@@ -190,26 +190,9 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       for (int r = 0; r < 16; ++r)
         if (kv0 + 32 * kb + 16 * hh + r >= skv) sacc[kb][r] = -INFINITY;
   };
-  auto softmax = [&]() {
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) {
-      mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
-      mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
-    }
-    float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
-    mx = partner_max(mx) * c;
-    const float m_new = vmax(m_run, mx);
-    const bool need = m_new > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
+  // Weights E4M3-packed, with the tile's sum.  The tile's 32 weights per lane
+  // are summed on their own before joining the running sum (see attn_fwd).
+  auto exps = [&]() __attribute__((always_inline)) -> float {
     const float neg_m = -m_run;
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
@@ -223,7 +206,39 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       lt1 += p1 + p3;
       pk[w] = pack4_fp8(p0, p1, p2, p3);
     }
-    l_run += lt0 + lt1;
+    return lt0 + lt1;
+  };
+  // The row max only matters when a weight against the running max would
+  // exceed 2^8 (the lazy-rescale threshold); then the lane's tile sum does
+  // too, or is not finite (the first tile).  So the weights are formed
+  // against the running max first, and only a wave with such a lane takes
+  // the row max, rescales and forms them again: the same result as always
+  // taking the max, with about 20 fewer instructions per tile.
+  auto softmax = [&]() __attribute__((always_inline)) {
+    float lt = exps();
+    if (__any(!(lt <= 256.0f))) {
+      float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+      for (int r = 1; r < 15; r += 2) {
+        mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
+        mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+      }
+      float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+      mx = partner_max(mx) * c;
+      const float m_new = vmax(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      lt = exps();
+    }
+    l_run += lt;
   };
 
   // ---- MFMA phase: PV(t) on 4 d-blocks, then QK(t+1) on 2 key blocks x 2
