@@ -7,11 +7,13 @@
 // Parallelism > Merge phase" batched combine).  Rows whose LSEs are all -inf
 // (no keys in any partial) give O = 0 and LSE = -inf.
 //
-// HBM-bound stream.  One workgroup covers 64 consecutive sequence positions of
-// one (b, h): the 64 x n LSE values are read coalesced and turned into
-// normalised weights in LDS, then each 16-lane group streams one 256-byte
-// (D = 128) output row, reading the n partial rows it combines (non-temporal
-// loads and stores: each byte is touched once).
+// HBM-bound stream (non-temporal loads and stores: each byte is touched
+// once).  A workgroup takes 16 consecutive positions s of a group of heads of
+// one batch entry, so for contiguous (B, S, H, D) partials it reads and writes
+// one contiguous span per partial (LTX-2 scale: 0.109 ms, 70 % of HBM, against
+// 0.117 ms when a workgroup took 64 positions of one head and read 256-byte
+// rows 8 KB apart).  Its weights take n * heads * 16 floats of LDS, sized at
+// launch: a fixed 64 KB allowed only two workgroups per CU and ran 40 % slower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,61 +26,69 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kRows = 64;
+constexpr int kTok = 16;         // consecutive sequence positions per workgroup
 constexpr int kThreads = 256;
+constexpr int kLdsFloats = 16384;  // at most 64 KB of weights per workgroup
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
   bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a, int n_stiles) {
-  __shared__ float w_s[kMaxMerge][kRows];
+// One workgroup: kTok consecutive positions s x a group of hg heads of one
+// batch entry.  Phase 1 turns the n LSEs of each (h, s) into normalised
+// weights in LDS (per head, kTok consecutive LSEs are read together).  Phase 2
+// streams the token rows: for contiguous (B, S, H, D) partials a token's heads
+// are adjacent, so the workgroup reads and writes kTok * hg * D * 2 contiguous
+// bytes per partial, not scattered 256-byte rows.
+__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a, int n_stiles, int hg, int n_hgroups) {
+  extern __shared__ float w_s[];  // [n][hg][kTok], sized at launch
 
-  const int st = blockIdx.x % n_stiles;
-  const int bh = blockIdx.x / n_stiles;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
-  const int s0 = st * kRows;
+  int rest = blockIdx.x;
+  const int st = rest % n_stiles; rest /= n_stiles;
+  const int g = rest % n_hgroups;
+  const int b = rest / n_hgroups;
+  const int s0 = st * kTok, h0 = g * hg;
+  const int nh = min(hg, a.H - h0);
   const int tid = threadIdx.x;
-  const int64_t lse_row = ((int64_t)b * a.H + h) * a.S;
 
-  if (tid < kRows) {
-    const int s = s0 + tid;
-    if (s < a.S) {
-      float L[kMaxMerge];
-      float M = -INFINITY;
+  for (int p = tid; p < nh * kTok; p += kThreads) {
+    const int hl = p / kTok, sl = p % kTok;
+    const int s = s0 + sl;
+    if (s >= a.S) continue;
+    const int64_t li = ((int64_t)b * a.H + h0 + hl) * a.S + s;
+    float L[kMaxMerge];
+    float M = -INFINITY;
+    for (int i = 0; i < a.n; ++i) {
+      L[i] = a.lse_in[i][li];
+      M = fmaxf(M, L[i]);
+    }
+    if (M == -INFINITY) {
+      for (int i = 0; i < a.n; ++i) w_s[(i * hg + hl) * kTok + sl] = 0.0f;
+      if (a.lse_out) a.lse_out[li] = -INFINITY;
+    } else {
+      float sum = 0.0f;
       for (int i = 0; i < a.n; ++i) {
-        L[i] = a.lse_in[i][lse_row + s];
-        M = fmaxf(M, L[i]);
+        L[i] = expf(L[i] - M);
+        sum += L[i];
       }
-      if (M == -INFINITY) {
-        for (int i = 0; i < a.n; ++i) w_s[i][tid] = 0.0f;
-        if (a.lse_out) a.lse_out[lse_row + s] = -INFINITY;
-      } else {
-        float sum = 0.0f;
-        for (int i = 0; i < a.n; ++i) {
-          L[i] = expf(L[i] - M);
-          sum += L[i];
-        }
-        const float inv = 1.0f / sum;
-        for (int i = 0; i < a.n; ++i) w_s[i][tid] = L[i] * inv;
-        if (a.lse_out) a.lse_out[lse_row + s] = M + logf(sum);
-      }
+      const float inv = 1.0f / sum;
+      for (int i = 0; i < a.n; ++i) w_s[(i * hg + hl) * kTok + sl] = L[i] * inv;
+      if (a.lse_out) a.lse_out[li] = M + logf(sum);
     }
   }
   __syncthreads();
 
-  const int vpr = a.D >> 3;  // 16-byte vectors per row
-  const int rows_per_pass = kThreads / vpr;
-  const int c = tid % vpr;
-  if (tid >= rows_per_pass * vpr) return;
-  for (int row = tid / vpr; row < kRows; row += rows_per_pass) {
-    const int s = s0 + row;
-    if (s >= a.S) break;
+  const int vpr = a.D >> 3;          // 16-byte vectors per head row
+  const int vpt = nh * vpr;          // per token
+  const int ns = min(kTok, a.S - s0);
+  for (int q = tid; q < ns * vpt; q += kThreads) {
+    const int sl = q / vpt, r = q % vpt;
+    const int hl = r / vpr, c = r % vpr;
+    const int s = s0 + sl, h = h0 + hl;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < a.n; ++i) {
-      const float w = w_s[i][row];
+      const float w = w_s[(i * hg + hl) * kTok + sl];
       const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.o_in[i] + (int64_t)b * a.in_sb[i] +
                                                                  (int64_t)s * a.in_ss[i] + (int64_t)h * a.in_sh[i] + 8 * c));
 #pragma unroll
@@ -97,10 +107,15 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a,
 }  // namespace
 
 hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream) {
-  const int n_stiles = (a.S + kRows - 1) / kRows;
-  const int64_t nblk = (int64_t)n_stiles * a.H * a.B;
-  if (nblk > 0x7fffffff || a.D % 8 != 0 || a.D / 8 > kThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_stiles);
+  if (a.D % 8 != 0 || a.n < 1 || a.n > kMaxMerge) return hipErrorInvalidValue;
+  const int hg = min(a.H, kLdsFloats / (a.n * kTok));  // heads whose weights fit in LDS
+  const int n_hgroups = (a.H + hg - 1) / hg;
+  const int n_stiles = (a.S + kTok - 1) / kTok;
+  const int64_t nblk = (int64_t)n_stiles * n_hgroups * a.B;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  const size_t lds = (size_t)a.n * hg * kTok * sizeof(float);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg,
+                     n_hgroups);
   return hipGetLastError();
 }
 

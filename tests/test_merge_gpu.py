@@ -51,6 +51,21 @@ def test_random_partials(n):
         assert (om[1, 100:103, 2].float() == 0).all() and t.isneginf(lm[1, 2, 100:103]).all()
 
 
+def test_heads_split_into_groups():
+    # 16 partials x 70 heads: the weights of a 16-position tile of all heads do
+    # not fit the kernel's LDS budget, so heads are processed in groups
+    note("merge n=16, H=70 (head groups), ragged token tail")
+    t = torch()
+    n, B, S, H, D = 16, 1, 37, 70, 64
+    parts = [synth.normal_bf16((B, S, H, D), 70 + i, 1) for i in range(n)]
+    g = np.random.Generator(np.random.PCG64(71))
+    lses = [(g.standard_normal((B, H, S)) * 3).astype(np.float32) for _ in range(n)]
+    om, lm = lsd.attn_merge([to_dev(p) for p in parts], [t.from_numpy(x).cuda() for x in lses])
+    t.cuda.synchronize()
+    Om, Lm = ref.merge(parts, lses)
+    assert_attention_close(to_f64(om), Om, lm.cpu().numpy(), Lm, "head groups")
+
+
 def test_strided_views_guard_bands_and_determinism():
     note("merge strided + guards")
     t = torch()
