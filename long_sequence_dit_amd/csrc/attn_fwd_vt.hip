@@ -139,12 +139,12 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
 
   // ---- Staging.  Stage buffer s (s % kStages) holds K_{s+1} in the K region
   // and V_s in the V region: the two tiles G(s) reads.  Every load goes
-  // through a buffer descriptor per tile whose range ends with the last valid
-  // key, so lanes past it read (or write) zeros; tiles past the end get an
-  // empty range.
-  // K: direct loads, 1 KB of LDS per wave instruction.  LDS row rho holds key
-  // swap23(rho); its 16-byte chunks are XOR-swizzled by row so that 16 lanes
-  // reading one chunk of 16 rows hit distinct banks.
+  // through a buffer descriptor per tile; lanes out of its range write zeros.
+  // K: direct loads, 1 KB of LDS per wave instruction.  A K tile's range ends
+  // with the last valid key (rows past it are zero; tiles past the end get an
+  // empty range).  LDS row rho holds key swap23(rho); its 16-byte chunks are
+  // XOR-swizzled by row so that 16 lanes reading one chunk of 16 rows hit
+  // distinct banks.
   uint32_t k_voff[C::kDma];
 #pragma unroll
   for (int u = 0; u < C::kDma; ++u) {
@@ -203,8 +203,8 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   for (int c4 = 0; c4 < 4; ++c4)
     vfa[c4] = vregion + l32 * 128 + 16 * ((2 * c4 + hh) ^ ((l32 >> 1) & 7));
   constexpr int kVRowBlock = 32 * 128;  // bytes per 32 V^T rows
-  // Workgroup barrier that orders LDS accesses.  Loads in flight (into VGPRs
-  // or LDS) stay in flight across it: their completion is awaited explicitly.
+  // Workgroup barrier that orders LDS accesses.  Direct loads in flight stay
+  // in flight across it: each wave awaits its own with s_waitcnt vmcnt.
   auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   f32x16 oacc[C::kDBlocks];
@@ -349,13 +349,13 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
     }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");  // K_0 and stage 0 landed
     if ((skv & 7) != 0 && tid < D) {  // side chunk of channel d = tid
-      const int c_s = (skv & (kBlockN - 1)) >> 3, k0 = skv & ~7;
-      const uint16_t* src = vbase + (int64_t)tid * a.v_sd + k0;
+      const int c_s = (skv & (kBlockN - 1)) >> 3, key0 = skv & ~7;
+      const uint16_t* src = vbase + (int64_t)tid * a.v_sd + key0;
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (k0 + 2 * e < skv) ? src[2 * e] : 0u;
-        const uint32_t hi = (k0 + 2 * e + 1 < skv) ? src[2 * e + 1] : 0u;
+        const uint32_t lo = (key0 + 2 * e < skv) ? src[2 * e] : 0u;
+        const uint32_t hi = (key0 + 2 * e + 1 < skv) ? src[2 * e + 1] : 0u;
         w[e] = lo | (hi << 16);
       }
       *(u32x4*)(lds + C::kSide + tid * 128 + 16 * (c_s ^ ((tid >> 1) & 7))) = (u32x4){w[0], w[1], w[2], w[3]};
