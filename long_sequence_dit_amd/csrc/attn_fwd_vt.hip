@@ -288,15 +288,19 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   };
   // Stage t+3 (K_{t+4}, V_{t+3}) goes into the buffer stage t-1 used, free
   // once both groups have passed G(t-1).  At the end the wave waits for its
-  // own loads of stage t+1, which the next barrier publishes: stages t+2 and
-  // t+3 may stay in flight.
-  constexpr int kInFlight = (kStages - 2) * 2 * C::kDma;
+  // own loads of stage t+2 (only stage t+3 may stay in flight), so that stage
+  // t+2 is published before either group starts SM(t+2): each wave then reads
+  // the first kDist fragments of G(t) at the end of SM(t), before the barrier,
+  // and G(t) starts without waiting on LDS latency (2 % faster).
+  constexpr int kInFlight = (kStages - 3) * 2 * C::kDma;
+  u32x4 fr[kDist];
+  auto prefetch = [&](auto st) {
+#pragma unroll
+    for (int i = 0; i < kDist; ++i) fr[i] = frag(i, st);
+  };
   auto mfma_phase = [&](int t, auto st) {
     constexpr int S = decltype(st)::value;
     constexpr int kFree = (S + kStages - 1) % kStages;
-    u32x4 fr[kDist];
-#pragma unroll
-    for (int i = 0; i < kDist; ++i) fr[i] = frag(i, st);
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -328,9 +332,10 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   //   B: QK(0)       | SM(0) | G(0) | SM(1) | ...
   // G(t) reads stage t during intervals 2t+1 (A) and 2t+2 (B); each group loads
   // its half of stage t+3 during its G(t) into the buffer of stage t-1, whose
-  // last reader finished in interval 2t, and has its half of stage t+1 landed
-  // by the end of its G(t), before G(t+1) starts for either group.  K_0, read
-  // by QK(0) only, sits in the V buffer of stage 3, first loaded in G(0).
+  // last reader finished in interval 2t, and has its half of stage t+2 landed
+  // by the end of its G(t) (interval 2t+2 at the latest), before SM(t+2)
+  // starts for either group.  K_0, read by QK(0) only, sits in the V buffer
+  // of stage 3, first loaded in G(0).
   // Past the last tile the loads have an empty range (they write zeros) into
   // buffers whose contents are never used.
   const int group = wave >> 2;
@@ -347,7 +352,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
       dma_k(s0 + 1, lds + s0 * C::kTileBytes);
       dma_v(s0, vregion + s0 * C::kVBytes);
     }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");  // K_0 and stage 0 landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");  // K_0, stages 0 and 1 landed
     if ((skv & 7) != 0 && tid < D) {  // side chunk of channel d = tid
       const int c_s = (skv & (kBlockN - 1)) >> 3, key0 = skv & ~7;
       const uint16_t* src = vbase + (int64_t)tid * a.v_sd + key0;
@@ -386,6 +391,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
       }
     }
     softmax();
+    prefetch(st);  // stage t was published before SM(t) began
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
     mfma_phase(t, st);
