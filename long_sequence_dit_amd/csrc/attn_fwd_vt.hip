@@ -275,7 +275,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   constexpr int kPvSteps = 4 * C::kDBlocks;  // (kb, ks, db)
   constexpr int kQkSteps = 2 * C::kDSteps;   // (kb, s2)
   constexpr int kSteps = kPvSteps + kQkSteps;
-  constexpr int kDist = 4;
+  constexpr int kDist = 6;
   auto frag = [&](int i, auto st) -> u32x4 {
     constexpr int S = decltype(st)::value;
     if (i < kPvSteps) {
