@@ -452,7 +452,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   // once every wave has left the loop) so that global stores write whole
   // 256-byte rows instead of 8-byte pieces of 32 different rows.
   __syncthreads();
-  constexpr int kRowO = D + 4;  // pitch (elements): rows land on distinct bank pairs
+  constexpr int kRowO = D + 8;  // pitch (elements): 16-byte aligned rows, 4-bank skew per row
   uint16_t* Ow = smem + wave * 32 * kRowO;
 #pragma unroll
   for (int db = 0; db < C::kDBlocks; ++db)
