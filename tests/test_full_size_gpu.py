@@ -1,6 +1,8 @@
 """The four full-size workloads on the GPU, in the launch configuration the
-benchmark times, checked on sampled query rows that the float64 oracle
-computes one by one against the full key set.
+benchmark times (V token-contiguous, the layout the relayout writes for the
+attention kernel), checked on sampled query rows that the float64 oracle
+computes one by one against the full key set.  LTX-2 and the unblocked Ring
+pass also run with V in the natural layout (the other attention kernel).
 
 Rows per (b, h): a seeded random sample plus the fixed rows {0, 1, 255, 256,
 first row of the ragged last 256-row tile, S_q - 1}."""
@@ -43,13 +45,39 @@ def check_rows(o_dev, lse_dev, q, k, v, heads, seed, what):
     note(f"{what}: worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} rel-rms {worst[2]:.3e}")
 
 
+def token_major(v_dev):
+    B, S, H, D = v_dev.shape
+    vt = lsd.v_token_major(B, S, H, D)
+    vt.copy_(v_dev)
+    return vt
+
+
 def test_ltx2_scale():
-    note("full LTX-2: B=1 S=24576 H=32 D=128, RMS-normalised Q/K")
+    note("full LTX-2: B=1 S=24576 H=32 D=128, RMS-normalised Q/K, V natural")
     t = torch()
     q, k, v = synth.ltx2_qkv()
     o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v))
     t.cuda.synchronize()
-    check_rows(o, lse, q, k, v, range(32), 1, "LTX-2")
+    check_rows(o, lse, q, k, v, range(0, 32, 2), 1, "LTX-2 (V natural)")
+
+
+def test_ltx2_bench_step():
+    note("full LTX-2 step as benchmarked: fused QKV -> relayout (V token-contiguous) -> 2 K/V blocks -> merge")
+    t = torch()
+    q, k, v = synth.ltx2_qkv()
+    B, S, H, D = q.shape
+    f = to_dev(np.stack([q, k, v], axis=2))
+    src = [[f[:, :, tt]] for tt in range(3)]
+    dq = t.empty((B, S, H, D), dtype=t.bfloat16, device="cuda")
+    dk = t.empty_like(dq)
+    dvt = lsd.v_token_major(B, S, H, D)
+    lsd.relayout_seq_to_head(src, 1, 0, dst=[dq, dk, dvt])
+    Sb = S // 2
+    parts = [lsd.attn_fwd(dq, dk[:, i * Sb:(i + 1) * Sb], dvt[:, i * Sb:(i + 1) * Sb]) for i in range(2)]
+    om, lm = lsd.attn_merge([o for o, _ in parts], [l for _, l in parts])
+    t.cuda.synchronize()
+    assert np.array_equal(to_bits(dvt), v), "relayout into token-contiguous V"
+    check_rows(om, lm, q, k, v, range(32), 1, "LTX-2 step")
 
 
 def test_ltx2_scale_key_padding_mask():
@@ -61,7 +89,8 @@ def test_ltx2_scale_key_padding_mask():
     v = v.copy()
     k[:, n:] = 0x7FC1
     v[:, n:] = 0x7FC1
-    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v), kv_lens=t.tensor([n], dtype=t.int32, device="cuda"))
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), token_major(to_dev(v)),
+                          kv_lens=t.tensor([n], dtype=t.int32, device="cuda"))
     t.cuda.synchronize()
     check_rows(o, lse, q, k[:, :n], v[:, :n], range(0, 32, 5), 11, "LTX-2 masked")
 
@@ -90,11 +119,12 @@ def test_wan_ulysses_share_relayout_then_attention():
     fused = synth.fused_qkv(B, S, H, D, seed=2)
     f = to_dev(fused)
     src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    hl = H // P
     for r in (0, 3):
         note(f"  relayout rank {r}")
-        qkv = lsd.relayout_seq_to_head(src, P, r)
+        dq = t.empty((B, S, hl, D), dtype=t.bfloat16, device="cuda")
+        qkv = lsd.relayout_seq_to_head(src, P, r, dst=[dq, t.empty_like(dq), lsd.v_token_major(B, S, hl, D)])
         t.cuda.synchronize()
-        hl = H // P
         for tt in range(3):
             got = to_bits(qkv[tt])
             exp = fused[:, :, tt, r * hl:(r + 1) * hl]   # concatenated shards = this rank's head slice
@@ -128,16 +158,17 @@ def test_ring_share_blocks_and_merge():
     Sb, H, D = 25_200, 40, 128
     q, k, v = synth.qkv(1, Sb, 3 * Sb, H, D, seed=3)
     dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    dvt = token_major(dv)
     outs, lses = [], []
     for i in range(3):
-        o, l = lsd.attn_fwd(dq, dk[:, i * Sb:(i + 1) * Sb], dv[:, i * Sb:(i + 1) * Sb])
+        o, l = lsd.attn_fwd(dq, dk[:, i * Sb:(i + 1) * Sb], dvt[:, i * Sb:(i + 1) * Sb])
         outs.append(o)
         lses.append(l)
     om, lm = lsd.attn_merge(outs, lses)
     ou, lu = lsd.attn_fwd(dq, dk, dv)
     t.cuda.synchronize()
     check_rows(om, lm, q, k, v, range(H), 3, "Ring merged")
-    check_rows(ou, lu, q, k, v, range(0, H, 5), 4, "Ring unblocked")
+    check_rows(ou, lu, q, k, v, range(0, H, 5), 4, "Ring unblocked (V natural)")
     # the merge against the oracle's merge of the same bf16 partials, on a row slab
     rows = slice(25_000, 25_200)
     Om, Lm = ref.merge([to_bits(o[:, rows]) for o in outs], [l[:, :, rows].cpu().numpy() for l in lses])
@@ -149,7 +180,7 @@ def test_ring_share_streaming_accumulate():
     t = torch()
     S = 25_200
     q, k, v = synth.qkv(1, S, 3 * S, 40, 128, seed=3)
-    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    dq, dk, dv = to_dev(q), to_dev(k), token_major(to_dev(v))
     o_acc = t.empty((1, S, 40, 128), dtype=t.float32, device="cuda")
     lse_acc = t.full((1, 40, S), float("-inf"), dtype=t.float32, device="cuda")
     o = t.empty((1, S, 40, 128), dtype=t.bfloat16, device="cuda")
@@ -165,6 +196,6 @@ def test_cosmos_long_sequence_with_outlier_keys():
     note("full Cosmos3-Super share: B=1 S=150000 H=16 D=128, 1% keys x4")
     t = torch()
     q, k, v, rows = synth.cosmos_qkv()
-    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), token_major(to_dev(v)))
     t.cuda.synchronize()
     check_rows(o, lse, q, k, v, range(16), 5, "Cosmos")
