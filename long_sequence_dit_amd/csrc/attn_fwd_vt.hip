@@ -29,7 +29,12 @@
 //   one streams MFMAs while the other does the softmax arithmetic.
 // * The row max is tracked lazily: O and l are rescaled only when a row's max
 //   grows by more than 2^8 (in the exp2 domain), which keeps exp2 arguments
-//   <= 8; the final O / l and LSE are exact for any reference max.
+//   <= 8; the final O / l and LSE are exact for any reference max.  A tile's
+//   max is taken only when its weights against the current reference could
+//   exceed 2^8, so most tiles skip it.
+// * The MFMA phase issues the next tiles' direct loads from inline assembly
+//   with every operand already scalar (M0 set by one scalar add), because each
+//   non-MFMA instruction in that phase delays the MFMA stream.
 // * blockIdx is remapped so that consecutive query tiles of one (b, h) land on
 //   the same XCD and share its L2 while streaming the same K/V.
 #include <hip/hip_runtime.h>
@@ -74,6 +79,20 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t vo
 #endif
 }
 
+// The same load issued from inline assembly with M0 computed by a scalar add
+// (LDS address = wbase + off): no vector-to-scalar moves on the way to M0.
+// The compiler does not see these loads; their completion is awaited with
+// explicit s_waitcnt vmcnt.
+__device__ inline void dma16_asm(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t wbase, uint32_t off,
+                                 uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+  const u32x4s rs = {r0, r1, r2, r3};
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               :: "s"(wbase), "s"(off), "v"(voff), "s"(rs) : "memory", "scc", "m0");
+#endif
+}
+
 // Key held by LDS row rho of a K tile: bits 2 and 3 swapped (an involution).
 __device__ inline int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
@@ -102,7 +121,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses in SGPRs
   const int l32 = lane & 31;
   const int hh = lane >> 5;  // lane half
 
@@ -191,6 +210,37 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
       dma16(r, dst + (wave * C::kDma + u) * 1024, off);
     }
   };
+  // Inside the loop the loads walk the tiles in order, so their tile pointers
+  // and key counts are running scalars, and every LDS destination is a scalar
+  // too: no vector-to-scalar moves feed M0 in the MFMA phase.
+  const int64_t k_tile_step = (int64_t)kBlockN * a.k_ss;
+  const uint16_t* k_next = kbase + kStages * k_tile_step;  // K_{t+4} in iteration t
+  int k_rows_next = skv - kStages * kBlockN;
+  // byte range of a full K tile (fits in 31 bits: the host keeps k_ss < 2^24)
+  const uint32_t k_full = (uint32_t)((kBlockN - 1) * (int)a.k_ss * 2 + 2 * D);
+  const uint32_t wbase = (uint32_t)(uintptr_t)lds + (uint32_t)wave * C::kDma * 1024;  // scalar
+  auto dma_k_next = [&](int buf_off) {
+    const int rows = k_rows_next;
+    const uint32_t n = rows >= kBlockN ? k_full : (rows > 0 ? (uint32_t)((rows - 1) * (int)a.k_ss * 2 + 2 * D) : 0u);
+    const uint64_t p = (uint64_t)(uintptr_t)k_next;
+#pragma unroll
+    for (int u = 0; u < C::kDma; ++u)
+      dma16_asm((uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, n, 0x00020000u, wbase, buf_off + u * 1024, k_voff[u]);
+    k_next += k_tile_step;
+    k_rows_next -= kBlockN;
+  };
+  const uint16_t* v_next = vbase + (kStages - 1) * kBlockN;  // V_{t+3} in iteration t
+  int v_key_next = (kStages - 1) * kBlockN;
+  auto dma_v_next = [&](int buf_off) {
+    const uint64_t p = (uint64_t)(uintptr_t)v_next;
+#pragma unroll
+    for (int u = 0; u < C::kDma; ++u) {
+      const uint32_t off = (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u;
+      dma16_asm((uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)vt_range, 0x00020000u, wbase, buf_off + u * 1024, off);
+    }
+    v_next += kBlockN;
+    v_key_next += kBlockN;
+  };
   // Each lane's fragment addresses (row l32), before stage and row-block
   // offsets: kfa[s2] for QK step s2, vfa[2 kb + ks] for the PV keys
   // 32 kb + 16 ks + 8 hh .. + 7.
@@ -227,31 +277,11 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
         if (j >= skv) sacc[kb][r] = -INFINITY;
       }
   };
-  auto softmax = [&]() {
-    // two chains of 3-input maxima (one instruction per two scores)
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) {
-      mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
-      mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
-    }
-    float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
-    mx = partner_max(mx) * c;
-    const float m_new = vmax(m_run, mx);
-    const bool need = m_new > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // P = exp2(S c - m) rounded to bf16.  The tile's 32 weights are summed on
-    // their own before joining the running sum: added one by one to a sum
-    // dominated by a few large weights (outlier keys), the many small ones
-    // would fall below half an ulp and be lost.
+  // P = exp2(S c - m) rounded to bf16, with m the current reference max.  The
+  // tile's 32 weights are summed on their own before joining the running sum:
+  // added one by one to a sum dominated by a few large weights (outlier keys),
+  // the many small ones would fall below half an ulp and be lost.
+  auto exps = [&]() __attribute__((always_inline)) -> float {
     const float neg_m = -m_run;
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
@@ -264,7 +294,47 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
         lt1 += p1;
         pk[kb][r >> 1] = pack_bf16(p0, p1);
       }
-    l_run += lt0 + lt1;
+    return lt0 + lt1;
+  };
+  static_assert(kRescaleThreshold == 8.0f, "the fast path bound below is 2^threshold");
+  auto softmax = [&]() __attribute__((always_inline)) {
+    // Fast path: weights against the current reference max.  Only when some
+    // lane's weights may exceed 2^8 (their sum does, or is not finite) is the
+    // row max taken: lazy rescale as described above, then the weights again.
+    // Either way every weight used is at most 2^8 times the reference.
+    float lt = exps();
+    if (__any(!(lt <= 256.0f))) {
+      // two chains of 3-input maxima (one instruction per two scores)
+      float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+      for (int r = 1; r < 15; r += 2) {
+        mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
+        mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+      }
+      float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+      mx = partner_max(mx) * c;
+      const float m_new = vmax(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      lt = exps();
+    }
+    l_run += lt;
+    // the weights and the sum are complete here, before the barrier that ends
+    // this phase (otherwise the compiler may sink their arithmetic into the
+    // MFMA phase)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[kb][i]));
+    asm volatile("" ::"v"(l_run));
   };
 
   // ---- MFMA phase G(t) = PV(t) then QK(t+1), as a fixed list of steps.  Step
@@ -317,8 +387,8 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
         const f32x16 acc_in = (s2 == 0) ? (f32x16){} : sacc[kb];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur), qreg[s2], acc_in, 0, 0, 0);
       }
-      if (i == 4) dma_k(t + kStages, lds + kFree * C::kTileBytes);
-      if (i == 12) dma_v(t + kStages - 1, vregion + kFree * C::kVBytes);
+      if (i == 4) dma_k_next(kFree * C::kTileBytes);
+      if (i == 12) dma_v_next(C::kVRegion + kFree * C::kVBytes);
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
