@@ -26,7 +26,9 @@
 //   one streams MFMAs while the other does the softmax arithmetic.
 // * The row max is tracked lazily: O and l are rescaled only when a row's max
 //   grows by more than 2^8 (in the exp2 domain), which keeps exp2 arguments
-//   <= 8; the final O / l and LSE are exact for any reference max.
+//   <= 8; the final O / l and LSE are exact for any reference max.  A tile's
+//   max is taken only when its weights against the current reference could
+//   exceed 2^8, so most tiles skip it.
 // * blockIdx is remapped so that consecutive query tiles of one (b, h) land on
 //   the same XCD and share its L2 while streaming the same K/V.
 #include <hip/hip_runtime.h>
@@ -218,31 +220,11 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
         if (j >= skv) sacc[kb][r] = -INFINITY;
       }
   };
-  auto softmax = [&]() {
-    // two chains of 3-input maxima (one instruction per two scores)
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) {
-      mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
-      mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
-    }
-    float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
-    mx = partner_max(mx) * c;
-    const float m_new = vmax(m_run, mx);
-    const bool need = m_new > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // P = exp2(S c - m) rounded to bf16.  The tile's 32 weights are summed on
-    // their own before joining the running sum: added one by one to a sum
-    // dominated by a few large weights (outlier keys), the many small ones
-    // would fall below half an ulp and be lost.
+  // P = exp2(S c - m) rounded to bf16, with m the current reference max.  The
+  // tile's 32 weights are summed on their own before joining the running sum:
+  // added one by one to a sum dominated by a few large weights (outlier keys),
+  // the many small ones would fall below half an ulp and be lost.
+  auto exps = [&]() __attribute__((always_inline)) -> float {
     const float neg_m = -m_run;
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
@@ -255,7 +237,47 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
         lt1 += p1;
         pk[kb][r >> 1] = pack_bf16(p0, p1);
       }
-    l_run += lt0 + lt1;
+    return lt0 + lt1;
+  };
+  static_assert(kRescaleThreshold == 8.0f, "the fast path bound below is 2^threshold");
+  auto softmax = [&]() __attribute__((always_inline)) {
+    // Fast path: weights against the current reference max.  Only when some
+    // lane's weights may exceed 2^8 (their sum does, or is not finite) is the
+    // row max taken: lazy rescale as described above, then the weights again.
+    // Either way every weight used is at most 2^8 times the reference.
+    float lt = exps();
+    if (__any(!(lt <= 256.0f))) {
+      // two chains of 3-input maxima (one instruction per two scores)
+      float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+      for (int r = 1; r < 15; r += 2) {
+        mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
+        mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+      }
+      float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+      mx = partner_max(mx) * c;
+      const float m_new = vmax(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      lt = exps();
+    }
+    l_run += lt;
+    // the weights and the sum are complete here, before the barrier that ends
+    // this phase (otherwise the compiler may sink their arithmetic into the
+    // MFMA phase)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[kb][i]));
+    asm volatile("" ::"v"(l_run));
   };
 
   // ---- MFMA phase G(t) = PV(t) then QK(t+1), as a fixed list of steps.  Step
