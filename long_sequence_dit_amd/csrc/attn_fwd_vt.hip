@@ -83,13 +83,12 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t vo
 // (LDS address = wbase + off): no vector-to-scalar moves on the way to M0.
 // The compiler does not see these loads; their completion is awaited with
 // explicit s_waitcnt vmcnt.
-__device__ inline void dma16_asm(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t wbase, uint32_t off,
-                                 uint32_t voff) {
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+template <int kOff>
+__device__ inline void dma16_asm(const u32x4s& rs, uint32_t wbase, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
-  const u32x4s rs = {r0, r1, r2, r3};
   asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
-               :: "s"(wbase), "s"(off), "v"(voff), "s"(rs) : "memory", "scc", "m0");
+               :: "s"(wbase), "i"(kOff), "v"(voff), "s"(rs) : "memory", "scc", "m0");
 #endif
 }
 
@@ -214,31 +213,37 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   // and key counts are running scalars, and every LDS destination is a scalar
   // too: no vector-to-scalar moves feed M0 in the MFMA phase.
   const int64_t k_tile_step = (int64_t)kBlockN * a.k_ss;
-  const uint16_t* k_next = kbase + kStages * k_tile_step;  // K_{t+4} in iteration t
+  // buffer descriptors of the next K and V^T tiles, advanced in place
+  const uint64_t k_first = (uint64_t)(uintptr_t)(kbase + kStages * k_tile_step);  // K_{t+4} in iteration t
+  u32x4s rk = {(uint32_t)k_first, (uint32_t)(k_first >> 32) & 0xffffu, 0u, 0x00020000u};
+  const uint64_t k_step = (uint64_t)k_tile_step * 2;
   int k_rows_next = skv - kStages * kBlockN;
   // byte range of a full K tile (fits in 31 bits: the host keeps k_ss < 2^24)
   const uint32_t k_full = (uint32_t)((kBlockN - 1) * (int)a.k_ss * 2 + 2 * D);
   const uint32_t wbase = (uint32_t)(uintptr_t)lds + (uint32_t)wave * C::kDma * 1024;  // scalar
-  auto dma_k_next = [&](int buf_off) {
+  auto advance = [](u32x4s& r, uint64_t step) {  // 48-bit base: the high word stays below 2^16
+    const uint64_t p = (((uint64_t)r[1] << 32) | r[0]) + step;
+    r[0] = (uint32_t)p;
+    r[1] = (uint32_t)(p >> 32);
+  };
+  auto dma_k_next = [&](auto off_c) {
+    constexpr int kOff = decltype(off_c)::value;
     const int rows = k_rows_next;
-    const uint32_t n = rows >= kBlockN ? k_full : (rows > 0 ? (uint32_t)((rows - 1) * (int)a.k_ss * 2 + 2 * D) : 0u);
-    const uint64_t p = (uint64_t)(uintptr_t)k_next;
-#pragma unroll
-    for (int u = 0; u < C::kDma; ++u)
-      dma16_asm((uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, n, 0x00020000u, wbase, buf_off + u * 1024, k_voff[u]);
-    k_next += k_tile_step;
+    rk[2] = rows >= kBlockN ? k_full : (rows > 0 ? (uint32_t)((rows - 1) * (int)a.k_ss * 2 + 2 * D) : 0u);
+    dma16_asm<kOff>(rk, wbase, k_voff[0]);
+    if constexpr (C::kDma > 1) dma16_asm<kOff + 1024>(rk, wbase, k_voff[1]);
+    advance(rk, k_step);
     k_rows_next -= kBlockN;
   };
-  const uint16_t* v_next = vbase + (kStages - 1) * kBlockN;  // V_{t+3} in iteration t
+  const uint64_t v_first = (uint64_t)(uintptr_t)(vbase + (kStages - 1) * kBlockN);  // V_{t+3} in iteration t
+  u32x4s rv = {(uint32_t)v_first, (uint32_t)(v_first >> 32) & 0xffffu, (uint32_t)vt_range, 0x00020000u};
   int v_key_next = (kStages - 1) * kBlockN;
-  auto dma_v_next = [&](int buf_off) {
-    const uint64_t p = (uint64_t)(uintptr_t)v_next;
-#pragma unroll
-    for (int u = 0; u < C::kDma; ++u) {
-      const uint32_t off = (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u;
-      dma16_asm((uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)vt_range, 0x00020000u, wbase, buf_off + u * 1024, off);
-    }
-    v_next += kBlockN;
+  auto dma_v_next = [&](auto off_c) {
+    constexpr int kOff = decltype(off_c)::value;
+    auto voff = [&](int u) { return (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u; };
+    dma16_asm<kOff>(rv, wbase, voff(0));
+    if constexpr (C::kDma > 1) dma16_asm<kOff + 1024>(rv, wbase, voff(1));
+    advance(rv, (uint64_t)kBlockN * 2);
     v_key_next += kBlockN;
   };
   // Each lane's fragment addresses (row l32), before stage and row-block
@@ -387,8 +392,8 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
         const f32x16 acc_in = (s2 == 0) ? (f32x16){} : sacc[kb];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur), qreg[s2], acc_in, 0, 0, 0);
       }
-      if (i == 4) dma_k_next(kFree * C::kTileBytes);
-      if (i == 12) dma_v_next(C::kVRegion + kFree * C::kVBytes);
+      if (i == 4) dma_k_next(std::integral_constant<int, kFree * C::kTileBytes>{});
+      if (i == 12) dma_v_next(std::integral_constant<int, C::kVRegion + kFree * C::kVBytes>{});
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
@@ -413,6 +418,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  static_assert(C::kDma <= 2, "one or two direct loads per wave and tile");
   static_assert(kStages == 4, "the main loop is unrolled for four stage buffers");
   uint8_t* const k0 = vregion + (kStages - 1) * C::kVBytes;
   dma_k(0, k0);
