@@ -7,6 +7,8 @@ token-contiguous kernel itself is bit-reproducible across row pitches and
 padding contents.  Row padding and masked keys hold NaN bit patterns, so a read
 of any of them would poison the output."""
 
+import math
+
 import numpy as np
 import pytest
 
@@ -149,3 +151,64 @@ def test_token_major_v_accumulate(D):
     V = np.concatenate([vh for _, vh in host], axis=1)
     O, L = ref.attention(qh, K, V)
     assert_attention_close(to_f64(res[1][2]), O, res[1][1].cpu().numpy(), L, "accumulate token-major")
+
+
+def growing_logit_keys(S_kv, H, D, steps, seed):
+    """Q rows all ones; the keys of tile i (64 keys) are a_i plus small noise in
+    every channel, with a_i chosen so that the scaled logit (in log2 units)
+    moves by steps[i % len(steps)] from one tile to the next.  Increments above
+    8 make the kernels take the row max and rescale (the slow path); smaller
+    ones keep the weights below 2^8 against the old reference (the fast path)."""
+    scale_log2 = math.log2(math.e) / math.sqrt(D)
+    per_unit = scale_log2 * D  # logit per unit of a with Q = 1
+    rng = np.random.default_rng(seed)
+    level, a = 0.0, np.empty(S_kv, np.float32)
+    for i in range((S_kv + 63) // 64):
+        level += steps[i % len(steps)]
+        a[64 * i:64 * (i + 1)] = level / per_unit
+    k = a[None, :, None, None] + rng.normal(0.0, 0.02, (1, S_kv, H, D)).astype(np.float32)
+    return synth.f32_to_bf16_bits(k.astype(np.float32))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("steps", [(9.0, 2.0, 12.0, 0.5, 7.5), (-3.0, 10.0, -20.0, 8.5)])
+def test_rescale_paths_both_layouts(D, steps):
+    """Row maxima that jump by more than 2^8 between tiles (row max taken, O
+    and l rescaled) alternating with tiles whose weights stay below 2^8 of the
+    old reference (max skipped), and falling maxima: both kernels against the
+    oracle."""
+    note(f"rescale paths D={D} steps={steps}")
+    t = torch()
+    B, S_q, S_kv, H = 1, 289, 64 * 12 + 17, 2
+    one = synth.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    qh = np.full((B, S_q, H, D), one, dtype=np.uint16)
+    kh = growing_logit_keys(S_kv, H, D, steps, 1501 + D)
+    vh = synth.normal_bf16((B, S_kv, H, D), 1502 + D, 1)
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
+    o1, l1 = lsd.attn_fwd(q, k, v)
+    o2, l2 = lsd.attn_fwd(q, k, token_major(v))
+    t.cuda.synchronize()
+    O, L = ref.attention(qh, kh, vh)
+    assert_attention_close(to_f64(o1), O, l1.cpu().numpy(), L, "natural V")
+    assert_attention_close(to_f64(o2), O, l2.cpu().numpy(), L, "token-major V")
+
+
+def test_token_major_v_dominant_logit_one_hot_bit_exact():
+    """One key per head dominates (logit 4 sqrt(D) above the others), late in
+    the sequence: the output is that key's V row, bit for bit."""
+    note("token-major V dominant logit")
+    S, D, H = 1000, 128, 2
+    two = synth.f32_to_bf16_bits(np.array([2.0], np.float32))[0]
+    q = np.full((1, 300, H, D), two, dtype=np.uint16)
+    k = np.zeros((1, S, H, D), dtype=np.uint16)
+    js = [777, 3]
+    for h in range(H):
+        k[0, js[h], h] = two
+    v = synth.normal_bf16((1, S, H, D), 13, 3)
+    t = torch()
+    o, lse = lsd.attn_fwd(to_dev(q), to_dev(k), token_major(to_dev(v)))
+    t.cuda.synchronize()
+    ob = to_bits(o)
+    for h in range(H):
+        assert np.array_equal(ob[0, :, h], np.broadcast_to(v[0, js[h], h], (300, D)))
+    assert np.abs(lse.cpu().numpy() - 4.0 * math.sqrt(D)).max() <= 1e-3
