@@ -468,7 +468,10 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
     }
     softmax();
     prefetch(st);  // stage t was published before SM(t) began
-    lds_barrier();
+    // No LDS wait before this barrier: the wave has written no LDS in SM(t),
+    // and its prefetch reads of stage t need not land before the other group
+    // proceeds (nobody writes that buffer until both groups have left G(t)).
+    asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_s_setprio(1);
     mfma_phase(t, st);
     __builtin_amdgcn_s_setprio(0);
