@@ -81,7 +81,8 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t vo
 
 // The same load issued from inline assembly with M0 computed by a scalar add
 // (LDS address = wbase + off): no vector-to-scalar moves on the way to M0.
-// The compiler does not see these loads; their completion is awaited with
+// One wait state separates the M0 write from the load that reads it.  The
+// compiler does not see these loads; their completion is awaited with
 // explicit s_waitcnt vmcnt.
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 template <int kOff>
@@ -220,7 +221,9 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   int k_rows_next = skv - kStages * kBlockN;
   // byte range of a full K tile (fits in 31 bits: the host keeps k_ss < 2^24)
   const uint32_t k_full = (uint32_t)((kBlockN - 1) * (int)a.k_ss * 2 + 2 * D);
-  const uint32_t wbase = (uint32_t)(uintptr_t)lds + (uint32_t)wave * C::kDma * 1024;  // scalar
+  // this wave's 1 KB slots of a tile (the low 32 bits of a flat pointer into
+  // LDS are the LDS address); scalar, since wave is
+  const uint32_t wbase = (uint32_t)(uintptr_t)lds + (uint32_t)wave * C::kDma * 1024;
   auto advance = [](u32x4s& r, uint64_t step) {  // 48-bit base: the high word stays below 2^16
     const uint64_t p = (((uint64_t)r[1] << 32) | r[0]) + step;
     r[0] = (uint32_t)p;
