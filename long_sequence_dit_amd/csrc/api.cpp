@@ -535,6 +535,8 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
   if (tok_units > 0x7fffffff)
     return fail(LSD_EUNSUPPORTED, "%s: %lld token-contiguous tiles exceed 2^31-1", fn, (long long)tok_units);
   if ((s = check_device()) != LSD_OK) return s;
+  if (a.n_tensors > 0 && at.n_tensors > 0 && !a.inverse && lsd::relayout_runs(a) > 0)
+    return launched(lsd::launch_relayout_both(a, at, (hipStream_t)stream), fn);
   if (a.n_tensors > 0 && (s = launched(lsd::launch_relayout(a, (hipStream_t)stream), fn)) != LSD_OK) return s;
   if (at.n_tensors > 0) return launched(lsd::launch_relayout_tok(at, (hipStream_t)stream), fn);
   return ok();

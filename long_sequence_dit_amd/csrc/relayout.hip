@@ -23,7 +23,9 @@
 // stores (non-temporal ones made it 6 % slower).  Run indices are wave-uniform,
 // so the per-run address arithmetic (tensor, shard, token) stays in scalar
 // registers, in 32 bits (the host checks the run count).  Runs are numbered so
-// that consecutive runs write consecutive destination bytes.
+// that consecutive runs write consecutive destination bytes.  A forward call
+// that writes some tensors token-contiguous (below) runs both kinds of
+// workgroup in one launch, interleaved.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,14 +41,14 @@ constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kUnroll = 4;  // 16-byte vectors per lane in flight per pass
 
 template <bool kInverse>
-__global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a, int n_runs) {
+__device__ __attribute__((always_inline)) void copy_body(const RelayoutArgs& a, int n_runs, int block, int nblocks) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int runs_per_token = a.H_loc / a.heads_per_run;
   const int vpr = a.heads_per_run * a.D / 8;  // vectors per run
-  const int stride = (int)gridDim.x * kWavesPerBlock;
+  const int stride = nblocks * kWavesPerBlock;
 
-  for (int run = (int)blockIdx.x * kWavesPerBlock + wave; run < n_runs; run += stride) {
+  for (int run = block * kWavesPerBlock + wave; run < n_runs; run += stride) {
     const int jr = run % runs_per_token;
     const int tok = run / runs_per_token;
     const int j0 = jr * a.heads_per_run;
@@ -102,6 +104,11 @@ __global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a
   }
 }
 
+template <bool kInverse>
+__global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a, int n_runs) {
+  copy_body<kInverse>(a, n_runs, (int)blockIdx.x, (int)gridDim.x);
+}
+
 // Forward relayout into a token-contiguous destination (each channel's
 // P*S_loc tokens one row of pitch dst_sd):
 //   dst[t][b, p*S_loc + s, j, d] = src[t][p][b, s, rank*H_loc + j, d]
@@ -115,9 +122,9 @@ __global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a
 // element by element, so row padding is never touched.
 constexpr int kTokWavesPerBlock = 4;
 
-__global__ void __launch_bounds__(64 * kTokWavesPerBlock) relayout_tok_kernel(const RelayoutArgs a, int n_units) {
+__device__ __attribute__((always_inline)) void tok_body(const RelayoutArgs& a, int n_units, int block) {
   const int lane = threadIdx.x & 63;
-  const int unit = (int)blockIdx.x * kTokWavesPerBlock + (int)(threadIdx.x >> 6);
+  const int unit = block * kTokWavesPerBlock + (int)(threadIdx.x >> 6);
   if (unit >= n_units) return;
   const int S = a.P * a.S_loc;
   const int n_tblk = (S + 63) / 64;
@@ -164,7 +171,37 @@ __global__ void __launch_bounds__(64 * kTokWavesPerBlock) relayout_tok_kernel(co
   }
 }
 
+__global__ void __launch_bounds__(64 * kTokWavesPerBlock) relayout_tok_kernel(const RelayoutArgs a, int n_units) {
+  tok_body(a, n_units, (int)blockIdx.x);
+}
+
+// Both in one launch: block i is a transposing block when floor((i+1) T / N)
+// > floor(i T / N) (T transposing blocks spread evenly over N), else a
+// copy block.
+__global__ void __launch_bounds__(kThreads) relayout_both_kernel(const RelayoutArgs a, const RelayoutArgs at, int n_runs,
+                                                                 int n_units, int n_total, int n_tok) {
+  const int i = (int)blockIdx.x;
+  const int t0 = (int)(((int64_t)i * n_tok) / n_total), t1 = (int)(((int64_t)(i + 1) * n_tok) / n_total);
+  if (t1 > t0) tok_body(at, n_units, t0);
+  else copy_body<false>(a, n_runs, i - t0, n_total - n_tok);
+}
+
 }  // namespace
+
+hipError_t launch_relayout_both(const RelayoutArgs& a, const RelayoutArgs& at, hipStream_t stream) {
+  const int64_t n_runs = relayout_runs(a);
+  const int64_t S = (int64_t)at.P * at.S_loc;
+  const int64_t n_units = (int64_t)at.n_tensors * at.B * at.H_loc * ((S + 63) / 64) * (at.D / 64);
+  if (n_runs > 0x7fffffff || n_units > 0x7fffffff || at.D % 64 != 0 || a.inverse || at.inverse)
+    return hipErrorInvalidValue;
+  const int64_t n_tok = (n_units + kTokWavesPerBlock - 1) / kTokWavesPerBlock;
+  int64_t n_copy = (n_runs + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (n_copy > 256 * 8 * 4) n_copy = 256 * 8 * 4;
+  if (n_copy + n_tok == 0) return hipSuccess;
+  hipLaunchKernelGGL(relayout_both_kernel, dim3((unsigned)(n_copy + n_tok)), dim3(kThreads), 0, stream, a, at, (int)n_runs,
+                     (int)n_units, (int)(n_copy + n_tok), (int)n_tok);
+  return hipGetLastError();
+}
 
 hipError_t launch_relayout_tok(const RelayoutArgs& a, hipStream_t stream) {
   const int64_t S = (int64_t)a.P * a.S_loc;
