@@ -374,8 +374,8 @@ def cpu_baseline(pipe, budget_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); the "
-              "sequence-parallel collectives are not part of it", file=sys.stderr)
+        print(f"bench.py: measures one GPU's share of the sequence-parallel work (asked for --gpus {args.gpus}); "
+              "the collectives between GPUs are not implemented, so only --gpus 1 runs", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
