@@ -168,3 +168,35 @@ def test_token_major_destination_feeds_attention():
     a, b = to_f64(o1), to_f64(o2)
     assert (np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6).all()
     assert float((l1 - l2).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("P,S_loc,D", [(2, 19, 64), (4, 33, 128)])
+def test_mixed_destinations_one_launch(P, S_loc, D):
+    """Q into a head-strided view (one copy run per head), K contiguous and V
+    token-contiguous in the same call: the forward call that runs copying and
+    transposing workgroups in one launch.  Every destination bit-exact, guard
+    slots and row padding untouched."""
+    note(f"relayout, mixed destinations in one launch: P={P} S_loc={S_loc} D={D}")
+    t = torch()
+    B, H = 2, 3 * P
+    Hl, S = H // P, P * S_loc
+    host = synth.random_bits16((B, S, 3, H, D), 501 + P + D)
+    f = to_dev(host)
+    src = [[f[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)] for tt in range(3)]
+    sentinel = -7777
+    big = t.full((B, S, 2 * Hl + 2, D), sentinel, dtype=t.int16, device="cuda")
+    q = big.view(t.bfloat16)[:, :, 1:1 + 2 * Hl:2]  # every other head slot
+    k = t.empty((B, S, Hl, D), dtype=t.bfloat16, device="cuda")
+    pitch = (S + 7) // 8 * 8 + 8
+    store = t.full((B, Hl, D, pitch), sentinel, dtype=t.int16, device="cuda")
+    vt = store.view(t.bfloat16).permute(0, 3, 1, 2)[:, :S]
+    for r in range(P):
+        lsd.relayout_seq_to_head(src, P, r, dst=[q, k, vt])
+        t.cuda.synchronize()
+        for tt, out in enumerate((q, k, vt)):
+            chunks = [host[:, p * S_loc:(p + 1) * S_loc, tt] for p in range(P)]
+            assert np.array_equal(to_bits(out), ref.relayout_seq_to_head(chunks, P, r)), (tt, r)
+        bb = big.cpu().numpy()
+        assert (bb[:, :, 0] == sentinel).all() and (bb[:, :, 2:2 * Hl + 1:2] == sentinel).all()
+        assert (bb[:, :, -1] == sentinel).all()
+        assert (store[..., S:].cpu().numpy() == sentinel).all(), "row padding written"
