@@ -8,12 +8,14 @@
 // (no keys in any partial) give O = 0 and LSE = -inf.
 //
 // HBM-bound stream (non-temporal loads and stores: each byte is touched
-// once).  A workgroup takes 16 consecutive positions s of a group of heads of
+// once).  A workgroup takes 2 consecutive positions s of a group of heads of
 // one batch entry, so for contiguous (B, S, H, D) partials it reads and writes
-// one contiguous span per partial (LTX-2 scale: 0.109 ms, 70 % of HBM, against
-// 0.117 ms when a workgroup took 64 positions of one head and read 256-byte
-// rows 8 KB apart).  Its weights take n * heads * 16 floats of LDS, sized at
-// launch: a fixed 64 KB allowed only two workgroups per CU and ran 40 % slower.
+// one contiguous span per partial.  Measured at LTX-2 scale (n = 2) and on the
+// Ring share (n = 3): 0.117 ms when a workgroup took 64 positions of one head
+// (256-byte rows 8 KB apart); 0.109 and 0.204 ms with 16 positions of all
+// heads; 0.105 and 0.188 ms with 2 (4 and 8 fall in between).  Its weights
+// take n * heads * 2 floats of LDS, sized at launch: a fixed 64 KB allowed
+// only two workgroups per CU and ran 40 % slower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,7 +28,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTok = 16;         // consecutive sequence positions per workgroup
+constexpr int kTok = 2;          // consecutive sequence positions per workgroup
 constexpr int kThreads = 256;
 constexpr int kLdsFloats = 16384;  // at most 64 KB of weights per workgroup
 
