@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
   }
 }
 
-// V: one workgroup per (b, h, 64 tokens).  Thread (token group g of 4 tokens,
+// V: one workgroup per (b, 64 tokens, h).  Thread (token group g of 4 tokens,
 // channel chunk c of 8 channels) converts a 4 x 8 block and writes, for each
 // of its 8 channels, the 4 tokens' codes as one dword of the transposed tile
 // in LDS ([d][64 tokens], pitch 80 B); then the tile leaves as 16-byte row
@@ -117,10 +117,11 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
 // readable and finite.
 __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_chunks) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 80];
-  const int chunk = blockIdx.x % n_chunks;
-  const int bh = blockIdx.x / n_chunks;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  // heads fastest: workgroups that run together read whole token rows (the
+  // cast 5 % faster than with token chunks fastest)
+  const int h = blockIdx.x % a.H;
+  const int chunk = (blockIdx.x / a.H) % n_chunks;
+  const int b = blockIdx.x / (a.H * n_chunks);
   const float inv = inv_scale(a.amax[((int64_t)2 * a.B + b) * a.H + h]);
   const uint16_t* src = a.src[2] + (int64_t)b * a.src_sb[2] + (int64_t)h * a.src_sh[2];
   const int s0 = chunk * kChunk;
