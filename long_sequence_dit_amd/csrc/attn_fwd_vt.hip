@@ -243,9 +243,14 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   int v_key_next = (kStages - 1) * kBlockN;
   auto dma_v_next = [&](auto off_c) {
     constexpr int kOff = decltype(off_c)::value;
-    auto voff = [&](int u) { return (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u; };
-    dma16_asm<kOff>(rv, wbase, voff(0));
-    if constexpr (C::kDma > 1) dma16_asm<kOff + 1024>(rv, wbase, voff(1));
+    if (v_key_next + kBlockN <= skv) {  // uniform: every chunk of the tile is valid
+      dma16_asm<kOff>(rv, wbase, v_voff[0]);
+      if constexpr (C::kDma > 1) dma16_asm<kOff + 1024>(rv, wbase, v_voff[1]);
+    } else {
+      auto voff = [&](int u) { return (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u; };
+      dma16_asm<kOff>(rv, wbase, voff(0));
+      if constexpr (C::kDma > 1) dma16_asm<kOff + 1024>(rv, wbase, voff(1));
+    }
     advance(rv, (uint64_t)kBlockN * 2);
     v_key_next += kBlockN;
   };
