@@ -69,6 +69,13 @@ __device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return (uint32_t)v;
 }
+// The same, writing over a dword whose old contents do not matter (both
+// halves are replaced), so no zero has to be moved in first.
+__device__ inline uint32_t pack4_fp8_over(uint32_t old, float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
 
 __device__ inline float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
@@ -180,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x16 sacc[2];
-  uint32_t pk[8];  // this tile's weights as E4M3, in PV operand order
+  uint32_t pk[8] = {};  // this tile's weights as E4M3, in PV operand order
 
   auto mask_tail = [&](int t) {
     const int kv0 = t * kBlockN;
@@ -202,9 +209,9 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
       const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 2], c, neg_m));
       const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 3], c, neg_m));
-      lt0 += p0 + p2;
-      lt1 += p1 + p3;
-      pk[w] = pack4_fp8(p0, p1, p2, p3);
+      lt0 = (w == 0) ? p0 + p2 : lt0 + (p0 + p2);  // no 0 + x: the first pair starts the sum
+      lt1 = (w == 0) ? p1 + p3 : lt1 + (p1 + p3);
+      pk[w] = pack4_fp8_over(pk[w], p0, p1, p2, p3);  // the previous tile's codes are dead
     }
     return lt0 + lt1;
   };
