@@ -233,8 +233,8 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
       for (int r = 0; r < 16; r += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, neg_m));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
-        lt0 += p0;
-        lt1 += p1;
+        lt0 = (kb == 0 && r == 0) ? p0 : lt0 + p0;  // no 0 + x: the first weights start the sums
+        lt1 = (kb == 0 && r == 0) ? p1 : lt1 + p1;
         pk[kb][r >> 1] = pack_bf16(p0, p1);
       }
     return lt0 + lt1;
