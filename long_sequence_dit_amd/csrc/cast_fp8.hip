@@ -81,30 +81,38 @@ __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs)
 
 __device__ inline float inv_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 1.0f; }
 
-// Q and K: one wave per (t in {0,1}, b, h, 64 tokens); 16-byte bf16 vectors in,
-// 8-byte code vectors out.
+// Q and K: one wave per (t in {0,1}, b, h, 64 tokens), heads fastest so that
+// waves running together read whole token rows; 16-byte bf16 vectors in,
+// 8-byte code vectors out.  All 16 loads of a lane are issued before any
+// conversion; rows past S re-read row S - 1 and are not stored.
 __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_chunks) {
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)2 * a.B * a.H * n_chunks;
   if (w >= n_waves) return;
-  const int chunk = (int)(w % n_chunks);
-  const int64_t tbh = w / n_chunks;
-  const int h = (int)(tbh % a.H);
-  const int b = (int)((tbh / a.H) % a.B);
-  const int t = (int)(tbh / ((int64_t)a.H * a.B));
+  const int h = (int)(w % a.H);
+  const int64_t rest = w / a.H;
+  const int chunk = (int)(rest % n_chunks);
+  const int b = (int)((rest / n_chunks) % a.B);
+  const int t = (int)(rest / ((int64_t)n_chunks * a.B));
   const float inv = inv_scale(a.amax[((int64_t)t * a.B + b) * a.H + h]);
-  const uint16_t* src = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t];
-  uint8_t* dst = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)h * a.dst_sh[t];
-  const int vec = lane & 15;
-  for (int i = lane >> 4; i < kChunk; i += 4) {
-    const int s = chunk * kChunk + i;
+  const uint16_t* src = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t] + 8 * (lane & 15);
+  uint8_t* dst = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)h * a.dst_sh[t] + 8 * (lane & 15);
+  const int s0 = chunk * kChunk + (lane >> 4);
+  u32x4 x[kChunk / 4];
+#pragma unroll
+  for (int u = 0; u < kChunk / 4; ++u) {
+    const int s = min(s0 + 4 * u, a.S - 1);
+    x[u] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[t]));
+  }
+#pragma unroll
+  for (int u = 0; u < kChunk / 4; ++u) {
+    const int s = s0 + 4 * u;
     if (s < a.S) {
-      const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[t] + 8 * vec));
       u32x2 c;
-      c[0] = pack4_fp8(bf16_lo(x[0]) * inv, bf16_hi(x[0]) * inv, bf16_lo(x[1]) * inv, bf16_hi(x[1]) * inv);
-      c[1] = pack4_fp8(bf16_lo(x[2]) * inv, bf16_hi(x[2]) * inv, bf16_lo(x[3]) * inv, bf16_hi(x[3]) * inv);
-      __builtin_nontemporal_store(c, (u32x2*)(dst + (int64_t)s * a.dst_ss[t] + 8 * vec));
+      c[0] = pack4_fp8(bf16_lo(x[u][0]) * inv, bf16_hi(x[u][0]) * inv, bf16_lo(x[u][1]) * inv, bf16_hi(x[u][1]) * inv);
+      c[1] = pack4_fp8(bf16_lo(x[u][2]) * inv, bf16_hi(x[u][2]) * inv, bf16_lo(x[u][3]) * inv, bf16_hi(x[u][3]) * inv);
+      __builtin_nontemporal_store(c, (u32x2*)(dst + (int64_t)s * a.dst_ss[t]));
     }
   }
 }
