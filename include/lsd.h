@@ -39,7 +39,9 @@
  *   fallback path: an unsupported request always fails loudly.
  *   lsd_last_error() returns a thread-local message for the last failure.
  * - Outputs may not overlap inputs (checked by address range): LSD_EINVAL.
- * - Results are deterministic: fixed reduction order, no atomics.
+ * - Results are deterministic: fixed reduction order.  The only atomic is
+ *   the FP8 cast's per-head absolute maximum (lsd_cast_qkv_fp8), a maximum
+ *   whose result does not depend on the order the updates land in.
  */
 #ifndef LSD_H
 #define LSD_H

@@ -88,15 +88,21 @@ def _torch():
 _16BIT = None
 
 
-def _view(t, name: str) -> View4:
+def _view(t, name: str, any16: bool = False) -> View4:
+    """C view of a 4-d GPU tensor.  Attention and merge operands must be
+    bfloat16 (the kernels read bf16 bits; an fp16 tensor would be silently
+    misread); the relayouts copy bit patterns and accept any 16-bit type
+    (``any16``)."""
     torch = _torch()
     global _16BIT
     if _16BIT is None:
         _16BIT = {torch.bfloat16, torch.int16, torch.uint16, torch.float16}
     if t.dim() != 4:
         raise ValueError(f"{name}: expected a 4-d (B, S, H, D) tensor, got {t.dim()}-d")
-    if t.dtype not in _16BIT:
-        raise ValueError(f"{name}: expected 16-bit elements (bfloat16), got {t.dtype}")
+    if any16 and t.dtype not in _16BIT:
+        raise ValueError(f"{name}: expected 16-bit elements, got {t.dtype}")
+    if not any16 and t.dtype != torch.bfloat16:
+        raise ValueError(f"{name}: expected bfloat16 elements, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name}: tensor must be in GPU memory (HIP library, no CPU path)")
     v = View4()
@@ -144,7 +150,7 @@ def attn_fwd(q, k, v, o=None, lse=None, scale: Optional[float] = None, return_ls
     torch = _torch()
     B, S_q, H, D = q.shape
     if o is None:
-        o = torch.empty((B, S_q, H, D), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
     vq, vk, vv, vo = _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o")
@@ -190,7 +196,7 @@ def attn_merge(o_parts: Sequence, lse_parts: Sequence, o=None, lse=None, return_
         raise ValueError("attn_merge: need as many LSE arrays as partial outputs (n >= 1)")
     B, S, H, D = o_parts[0].shape
     if o is None:
-        o = torch.empty((B, S, H, D), dtype=o_parts[0].dtype, device=o_parts[0].device)
+        o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=o_parts[0].device)
     if return_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=o.device)
     views = (View4 * n)(*[_view(t, f"o_parts[{i}]") for i, t in enumerate(o_parts)])
@@ -299,8 +305,9 @@ def relayout_seq_to_head(src: Sequence[Sequence], P: int, rank: int, dst: Option
             raise ValueError(f"relayout_seq_to_head: head count H={H} is not divisible by P={P}")
         dst = [torch.empty((B, P * S_loc, H // P, D), dtype=src[0][0].dtype, device=src[0][0].device)
                for _ in range(nt)]
-    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{p}]") for t, s in enumerate(src) for p, c in enumerate(s)])
-    dv = (View4 * nt)(*[_view(d, f"dst[{t}]") for t, d in enumerate(dst)])
+    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{p}]", any16=True) for t, s in enumerate(src)
+                              for p, c in enumerate(s)])
+    dv = (View4 * nt)(*[_view(d, f"dst[{t}]", any16=True) for t, d in enumerate(dst)])
     st = lib().lsd_relayout_seq_to_head(nt, P, rank, sv, dv, _stream(src[0][0]))
     _check(st, "lsd_relayout_seq_to_head")
     return dst
@@ -324,8 +331,9 @@ def relayout_head_to_seq(src: Sequence[Sequence], P: int, rank: int, dst: Option
             raise ValueError(f"relayout_head_to_seq: sequence length S={S} is not divisible by P={P}")
         dst = [torch.empty((B, S // P, P * H_loc, D), dtype=src[0][0].dtype, device=src[0][0].device)
                for _ in range(nt)]
-    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{r}]") for t, s in enumerate(src) for r, c in enumerate(s)])
-    dv = (View4 * nt)(*[_view(d, f"dst[{t}]") for t, d in enumerate(dst)])
+    sv = (View4 * (nt * P))(*[_view(c, f"src[{t}][{r}]", any16=True) for t, s in enumerate(src)
+                              for r, c in enumerate(s)])
+    dv = (View4 * nt)(*[_view(d, f"dst[{t}]", any16=True) for t, d in enumerate(dst)])
     st = lib().lsd_relayout_head_to_seq(nt, P, rank, sv, dv, _stream(src[0][0]))
     _check(st, "lsd_relayout_head_to_seq")
     return dst

@@ -529,8 +529,11 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
   }
   a.heads_per_run = contiguous_heads ? (int)H_loc : 1;
   at.heads_per_run = 1;
-  if (lsd::relayout_runs(a) > 0x7fffffff)
-    return fail(LSD_EUNSUPPORTED, "%s: %lld copy runs exceed 2^31-1", fn, (long long)lsd::relayout_runs(a));
+  // The copy kernel indexes runs in 32-bit signed arithmetic and advances a
+  // wave's run index by about the run count (one wave per run), so the count
+  // must stay at or below 2^30 for `run + stride` to fit.
+  if (lsd::relayout_runs(a) > (int64_t)1 << 30)
+    return fail(LSD_EUNSUPPORTED, "%s: %lld copy runs exceed 2^30", fn, (long long)lsd::relayout_runs(a));
   const int64_t tok_units = (int64_t)at.n_tensors * B * H_loc * ((P * S_loc + 63) / 64) * (D / 64);
   if (tok_units > 0x7fffffff)
     return fail(LSD_EUNSUPPORTED, "%s: %lld token-contiguous tiles exceed 2^31-1", fn, (long long)tok_units);

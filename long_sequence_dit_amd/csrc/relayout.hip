@@ -22,7 +22,8 @@
 // that was just written and is partly still cached, so it keeps plain loads and
 // stores (non-temporal ones made it 6 % slower).  Run indices are wave-uniform,
 // so the per-run address arithmetic (tensor, shard, token) stays in scalar
-// registers, in 32 bits (the host checks the run count).  Runs are numbered so
+// registers, in 32 bits (the host keeps the run count at or below 2^30, so a
+// wave's run index plus the grid stride cannot overflow).  Runs are numbered so
 // that consecutive runs write consecutive destination bytes.  A forward call
 // that writes some tensors token-contiguous (below) runs both kinds of
 // workgroup in one launch.

@@ -11,7 +11,6 @@ from .ref import (  # noqa: F401
     bf16_bits_to_f64,
     attention,
     attention_rows,
-    attention_probs,
     merge,
     merge_two_logsigmoid,
     relayout_seq_to_head,

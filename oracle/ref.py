@@ -133,15 +133,6 @@ def attention_rows(q, k, v, b: int, h: int, rows: Iterable[int], scale=None, kv_
     return _attend_block(qh, kh, vh, sc)
 
 
-def attention_probs(q, k, b: int, h: int, rows: Iterable[int], scale=None):
-    """The softmax weight matrix p_ij of selected rows of one (batch, head)."""
-    rows = np.asarray(list(rows), dtype=np.int64)
-    sc = _default_scale(q.shape[3], scale)
-    s = (_as_f64(q[b, rows, h, :]) @ _as_f64(k[b, :, h, :]).T) * sc
-    e = np.exp(s - s.max(axis=1, keepdims=True))
-    return e / e.sum(axis=1, keepdims=True)
-
-
 def merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     """Exact log-sum-exp merge of n partial results over disjoint key spans.
 

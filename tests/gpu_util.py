@@ -50,16 +50,28 @@ def err_stats(o_gpu: np.ndarray, o_ref: np.ndarray):
     return float(d.max()), float(d.mean()), rel
 
 
-def assert_attention_close(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu=None, lse_ref=None, what=""):
+def lse_max_abs(lse_gpu, lse_ref, what="") -> float:
+    """Largest |LSE_gpu - LSE_ref|; entries that are -inf on both sides agree
+    (0), a -inf on one side only is a mismatch (raises)."""
+    lg = np.asarray(lse_gpu, dtype=np.float64)
+    lr = np.asarray(lse_ref, dtype=np.float64)
+    both_inf = np.isneginf(lg) & np.isneginf(lr)
+    with np.errstate(invalid="ignore"):   # -inf - -inf is masked out just below
+        d = np.where(both_inf, 0.0, np.abs(lg - lr))
+    assert np.all(np.isfinite(d)), f"{what}: LSE -inf/finite mismatch"
+    return float(d.max()) if d.size else 0.0
+
+
+def assert_attention_close(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu=None, lse_ref=None, what="",
+                           with_lse=False):
+    """The parity bar; returns (O max-abs, O mean-abs, O relative RMS) and,
+    with ``with_lse``, the LSE max-abs as a fourth value."""
     mx, mean, rel = err_stats(o_gpu, o_ref)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     assert mx <= O_MAX_ABS, f"{what}: O max-abs {mx:.3e} > {O_MAX_ABS}"
     assert mean <= O_MEAN_ABS, f"{what}: O mean-abs {mean:.3e} > {O_MEAN_ABS}"
+    dl = 0.0
     if lse_gpu is not None:
-        lg = np.asarray(lse_gpu, dtype=np.float64)
-        lr = np.asarray(lse_ref, dtype=np.float64)
-        both_inf = np.isneginf(lg) & np.isneginf(lr)
-        d = np.where(both_inf, 0.0, np.abs(lg - lr))
-        assert np.all(np.isfinite(d)), f"{what}: LSE -inf/finite mismatch"
-        assert d.max() <= LSE_MAX_ABS, f"{what}: LSE max-abs {d.max():.3e} > {LSE_MAX_ABS}"
-    return mx, mean, rel
+        dl = lse_max_abs(lse_gpu, lse_ref, what)
+        assert dl <= LSE_MAX_ABS, f"{what}: LSE max-abs {dl:.3e} > {LSE_MAX_ABS}"
+    return (mx, mean, rel, dl) if with_lse else (mx, mean, rel)

@@ -84,13 +84,11 @@ def pin_dominant_logit():
 
 
 def pin_rows_sum_to_one():
-    """Softmax rows are non-negative and sum to 1; V = 1 everywhere gives O = 1."""
+    """Softmax rows sum to 1: with V = 1 everywhere the output is exactly 1 for
+    every row (any weight that is lost, doubled or unnormalised moves it)."""
     B, Sq, Skv, H, D = 1, 19, 41, 2, 64
     q = _rand((B, Sq, H, D), 5)
     k = _rand((B, Skv, H, D), 6)
-    p = ref.attention_probs(q, k, 0, 1, range(Sq))
-    assert p.shape == (Sq, Skv)
-    assert np.all(p >= 0) and np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
     ones = np.full((B, Skv, H, D), _bits_of(1.0), dtype=np.uint16)
     O, _ = ref.attention(q, k, ones)
     assert np.allclose(O, 1.0, rtol=0, atol=1e-13), "V = 1 must give O = 1"

@@ -1,7 +1,13 @@
 """The C-ABI library (CPU only): it loads, exports every entry point that
 include/lsd.h declares, and rejects invalid requests on the host before any
 HIP call.  Pointers here are fake (aligned addresses that are never
-dereferenced): validation is pure address arithmetic."""
+dereferenced): validation is pure address arithmetic.
+
+A few cases check that a layout is *accepted*: such a call gets past
+validation to the device check, which fails where no GPU is visible.  On a
+machine with a GPU that call would go on to launch a kernel on the fake
+addresses, so those cases are skipped whenever a GPU is visible (the GPU
+parity tests exercise the same layouts with real memory there)."""
 
 import ctypes
 import os
@@ -15,6 +21,23 @@ from long_sequence_dit_amd import View4, LSD_EINVAL, LSD_EUNSUPPORTED
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lsd.h")
 
 BASE = 1 << 40  # fake, 16-byte aligned device addresses
+
+
+def gpu_visible() -> bool:
+    """True when a GPU is visible to this process (counting devices does not
+    initialise one)."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover - torch missing or broken
+        return os.path.exists("/dev/kfd")
+
+
+def skip_if_gpu(what: str) -> None:
+    """Guard a call whose arguments pass validation: with fake addresses it
+    may only run where the device check stops it (no GPU visible)."""
+    if gpu_visible():
+        pytest.skip(f"{what}: passes validation and would launch on fake addresses with a GPU visible")
 
 
 def declared_symbols():
@@ -307,10 +330,6 @@ def vt_view(addr, B, S, H, D, pitch):
 def test_attn_fwd_token_major_v_validation():
     q, k, _, o = good4(S_kv=300)
     B, S_kv, H, D = 1, 300, 2, 64
-    # accepted layout: validation passes, so the call reaches the device check
-    # (no GPU here) instead of failing on the view
-    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 304), o)
-    assert "v:" not in msg and "pitch" not in msg
     r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 296), o)
     assert r == LSD_EINVAL and "below S=300" in msg
     r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 308), o)
@@ -322,13 +341,23 @@ def test_attn_fwd_token_major_v_validation():
     # neither channels nor tokens unit-stride
     r, msg = attn(q, k, view(BASE + 2 * GB, (B, S_kv, H, D), [S_kv * H * D * 2, 2, S_kv * D * 2, 8]), o)
     assert r == LSD_EINVAL and "stride[3] must be 1" in msg
-    # a token-contiguous v may have a huge batch stride (the 2^24 limit is on k and natural v)
-    vt = view(BASE + 2 * GB, (B, S_kv, H, D), [1 << 30, 1, D * 304, 304])
-    r, msg = attn(q, k, vt, o)
-    assert "2^24" not in msg and "v:" not in msg
     # overlap with an output is still caught
     r, msg = attn(q, k, vt_view(BASE + 3 * GB, B, S_kv, H, D, 304), o)
     assert r == LSD_EINVAL and "overlaps" in msg
+
+
+def test_attn_fwd_token_major_v_accepted():
+    skip_if_gpu("accepted token-contiguous V layouts")
+    q, k, _, o = good4(S_kv=300)
+    B, S_kv, H, D = 1, 300, 2, 64
+    # accepted layout: validation passes, so the call reaches the device check
+    # (no GPU here) instead of failing on the view
+    r, msg = attn(q, k, vt_view(BASE + 2 * GB, B, S_kv, H, D, 304), o)
+    assert r != 0 and "v:" not in msg and "pitch" not in msg
+    # a token-contiguous v may have a huge batch stride (the 2^24 limit is on k and natural v)
+    vt = view(BASE + 2 * GB, (B, S_kv, H, D), [1 << 30, 1, D * 304, 304])
+    r, msg = attn(q, k, vt, o)
+    assert r != 0 and "2^24" not in msg and "v:" not in msg
 
 
 def test_relayout_token_major_destination_validation():
@@ -337,9 +366,10 @@ def test_relayout_token_major_destination_validation():
     S, Hl = P * S_loc, H // P
     def dsts(vt):
         return (View4 * 3)(view(BASE + 10 * GB, (B, S, Hl, D)), view(BASE + 11 * GB, (B, S, Hl, D)), vt)
-    ok_vt = vt_view(BASE + 12 * GB, B, S, Hl, D, 200)
-    r, msg = relayout(3, P, 0, src, dsts(ok_vt))
-    assert "dst" not in msg
+    if not gpu_visible():  # accepted: reaches the device check, which stops it without a GPU
+        ok_vt = vt_view(BASE + 12 * GB, B, S, Hl, D, 200)
+        r, msg = relayout(3, P, 0, src, dsts(ok_vt))
+        assert r != 0 and "dst" not in msg
     r, msg = relayout(3, P, 0, src, dsts(vt_view(BASE + 12 * GB, B, S, Hl, D, 192)))
     assert r == LSD_EINVAL and "below S=200" in msg
     r, msg = relayout(3, P, 0, src, dsts(view(BASE + 12 * GB, (B, S, Hl, D), [Hl * D * 200, 1, 104, 200])))
@@ -360,3 +390,21 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU memory"):
         lsd.attn_fwd(q, q, q)
+
+
+def test_python_binding_refuses_non_bf16_attention_and_merge_operands():
+    """fp16 (or int16) bits would be read as bf16 and give a silently wrong
+    result: attention and merge take bfloat16 only (checked before any device
+    work); the relayouts, pure bit copies, accept any 16-bit type."""
+    torch = pytest.importorskip("torch")
+    b = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    for dt in (torch.float16, torch.int16):
+        h = torch.zeros((1, 8, 1, 64), dtype=dt)
+        with pytest.raises(ValueError, match="bfloat16"):
+            lsd.attn_fwd(h, b, b)
+        with pytest.raises(ValueError, match="bfloat16"):
+            lsd.attn_fwd_accumulate(h, b, b, torch.zeros((1, 8, 1, 64)), torch.zeros((1, 1, 8)))
+        with pytest.raises(ValueError, match="bfloat16"):
+            lsd.attn_merge([h, b], [torch.zeros((1, 1, 8)), torch.zeros((1, 1, 8))])
+        with pytest.raises(ValueError, match="GPU memory"):   # passes the dtype check, stops at the device
+            lsd.relayout_seq_to_head([[h]], 1, 0, dst=[h.clone()])

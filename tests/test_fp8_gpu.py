@@ -42,6 +42,7 @@ def check_fp8(o, lse, q8, k8, v8, amax, heads, rows_fn, what, scale=None):
     D = q8.shape[3]
     sc = ref._default_scale(D, scale)
     worst = 0.0
+    worst_lse = 0.0
     errs, mags = [], []
     for b in range(q8.shape[0]):
         for h in heads:
@@ -66,13 +67,14 @@ def check_fp8(o, lse, q8, k8, v8, amax, heads, rows_fn, what, scale=None):
             assert ratio <= 1.0, f"{what} b={b} h={h}: error exceeds the FP8 bound (ratio {ratio:.3f})"
             dl = np.abs(lg[b, h, rows] - L)
             assert dl.max() <= 1e-3, f"{what} b={b} h={h}: LSE max-abs {dl.max():.3e}"
+            worst_lse = max(worst_lse, float(dl.max()))
             errs.append(err.ravel())
             mags.append(np.abs(O).ravel())
     if errs:
         e, m = np.concatenate(errs), np.concatenate(mags)
         assert e.mean() <= 0.05 * m.mean() + 1e-4, f"{what}: mean-abs {e.mean():.3e} vs mean|O| {m.mean():.3e}"
         note(f"{what}: worst bound ratio {worst:.3f}, mean-abs {e.mean():.3e} ({e.mean() / max(m.mean(), 1e-30):.2%} "
-             f"of mean |O|)")
+             f"of mean |O|), worst LSE max-abs {worst_lse:.3e}")
 
 
 def all_rows(S):
