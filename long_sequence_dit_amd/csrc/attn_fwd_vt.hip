@@ -498,16 +498,14 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   const float l_tot = partner_sum(l_run);
   const float inv = 1.0f / l_tot;
   constexpr float kLn2 = 0.69314718055994530942f;
-  float osc = inv;  // scale from oacc to the output values
+  const float osc = inv;  // scale from oacc to the output values
   if constexpr (kAcc) {
     // Merge with the running result of earlier key blocks (exact LSE merge,
     // fp32): with M = max(LSE_acc, LSE_blk) and w = exp(LSE - M),
     //   O_acc <- (w_acc O_acc + w_blk O_blk) / (w_acc + w_blk),
     //   LSE_acc <- M + ln(w_acc + w_blk).
     // LSE_blk is finite (the block has keys), so M is; rows with no history
-    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.  Each lane
-    // reads and writes its row's 16-byte runs of O_acc in the accumulator
-    // layout (channels 32 db + 8 g + 4 hh .. +3).
+    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.
     const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + qrow;
     const float lse_b = (m_run + __log2f(l_tot)) * kLn2;
     const float lse_a = qvalid ? a.lse_acc[lrow] : -INFINITY;
@@ -516,24 +514,49 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
     const float wb = expf(lse_b - mx);
     const float rs = 1.0f / (wa + wb);
     const float ca = wa * rs, cb = wb * rs * inv;
-    float* orow = a.o_acc + (((int64_t)b * a.S_q + qrow) * a.H + h) * D + 4 * hh;
+    if (hh == 0 && qvalid) a.lse_acc[lrow] = mx + logf(wa + wb);
+    // The block's weighted rows (w_blk O_blk / (w_acc + w_blk)) go through LDS
+    // (the K/V stage buffers are free once every wave has left the loop), so
+    // that the fp32 running O is read and written in whole 512-byte rows
+    // rather than 16-byte pieces of 32 rows.  Per wave: 32 rows of D floats
+    // (pitch D + 4) and the rows' history weights w_acc / (w_acc + w_blk).
+    __syncthreads();
+    constexpr int kRowA = D + 4;
+    static_assert(kWaves * (32 * kRowA + 32) * 4 <= C::kLdsBytes, "fp32 staging fits the stage buffers");
+    float* Aw = (float*)smem + wave * (32 * kRowA + 32);
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 prev = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (qvalid && wa > 0.0f) prev = *(const f32x4*)(orow + 32 * db + 8 * g);
-        f32x4 nv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          nv[e] = prev[e] * ca + oacc[db][4 * g + e] * cb;
-          oacc[db][4 * g + e] = nv[e];
-        }
-        if (qvalid) *(f32x4*)(orow + 32 * db + 8 * g) = nv;
+        const f32x4 w = {oacc[db][4 * g + 0] * cb, oacc[db][4 * g + 1] * cb, oacc[db][4 * g + 2] * cb,
+                         oacc[db][4 * g + 3] * cb};
+        *(f32x4*)(Aw + l32 * kRowA + 32 * db + 8 * g + 4 * hh) = w;
       }
-    if (hh == 0 && qvalid) a.lse_acc[lrow] = mx + logf(wa + wb);
-    osc = 1.0f;
-    if (a.o == nullptr) return;  // uniform: no bf16 output requested
+    if (hh == 0) Aw[32 * kRowA + l32] = ca;
+    __syncthreads();
+    // lane -> (row, 16-byte chunk of the row): 2 rows per pass at D = 128
+    constexpr int kCPR = D / 4;
+    constexpr int kRowsPerPass = 64 / kCPR;
+    const int ch = lane % kCPR;
+    const int row_base = qt * kBlockM + wave * 32;
+#pragma unroll 4
+    for (int r = lane / kCPR; r < 32; r += kRowsPerPass) {
+      const int row = row_base + r;
+      if (row >= a.S_q) break;  // rows past S_q only at the end of the wave's range
+      const float car = Aw[32 * kRowA + r];
+      f32x4 nv = *(const f32x4*)(Aw + r * kRowA + 4 * ch);
+      float* gp = a.o_acc + (((int64_t)b * a.S_q + row) * a.H + h) * D + 4 * ch;
+      if (car > 0.0f) {  // history exists (w_acc > 0): O_acc holds data
+        const f32x4 prev = *(const f32x4*)gp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nv[e] = __builtin_fmaf(prev[e], car, nv[e]);
+      }
+      *(f32x4*)gp = nv;
+      if (a.o != nullptr)
+        *(u32x2*)(a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh + 4 * ch) =
+            (u32x2){pack_bf16(nv[0], nv[1]), pack_bf16(nv[2], nv[3])};
+    }
+    return;
   }
   // Stage this wave's 32 x D output tile through LDS (the K/V buffers are free
   // once every wave has left the loop) so that global stores write whole
