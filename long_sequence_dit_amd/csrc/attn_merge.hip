@@ -15,7 +15,9 @@
 // (256-byte rows 8 KB apart); 0.109 and 0.204 ms with 16 positions of all
 // heads; 0.105 and 0.188 ms with 2 (4 and 8 fall in between).  Its weights
 // take n * heads * 2 floats of LDS, sized at launch: a fixed 64 KB allowed
-// only two workgroups per CU and ran 40 % slower.
+// only two workgroups per CU and ran 40 % slower.  Workgroups of 512 threads:
+// at n = 3 (the Ring share) 0.181 ms against 0.193 ms with 256 threads, at
+// n = 2 (LTX-2 scale) 0.108 against 0.111 ms.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,7 +31,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTok = 2;          // consecutive sequence positions per workgroup
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // 256 measured 5-7 % slower at n = 2 and 3, 1024 15 % slower at n = 3
 constexpr int kLdsFloats = 16384;  // at most 64 KB of weights per workgroup
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
