@@ -535,7 +535,7 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
   if (lsd::relayout_runs(a) > (int64_t)1 << 30)
     return fail(LSD_EUNSUPPORTED, "%s: %lld copy runs exceed 2^30", fn, (long long)lsd::relayout_runs(a));
   // transposing waves: 64-token blocks, counted in groups of 4 per (tensor, batch, head, 64 channels)
-  const int64_t tok_units = (int64_t)at.n_tensors * B * H_loc * (((P * S_loc + 63) / 64 + 3) / 4 * 4) * (D / 64);
+  const int64_t tok_units = (int64_t)at.n_tensors * B * H_loc * (((P * S_loc + 63) / 64 + 3) / 4 * 4) * ((D / 64 + 1) / 2);
   if (tok_units > 0x7fffffff)
     return fail(LSD_EUNSUPPORTED, "%s: %lld token-contiguous tiles exceed 2^31-1", fn, (long long)tok_units);
   if ((s = check_device()) != LSD_OK) return s;

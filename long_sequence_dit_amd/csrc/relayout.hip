@@ -114,14 +114,26 @@ __global__ void __launch_bounds__(kThreads) relayout_kernel(const RelayoutArgs a
 // P*S_loc tokens one row of pitch dst_sd):
 //   dst[t][b, p*S_loc + s, j, d] = src[t][p][b, s, rank*H_loc + j, d]
 // with the destination stored [b][j][d][token].  One wave moves 64 tokens x
-// 64 channels of one head: lane (c = lane % 8, g = lane / 8) loads 16 bytes
-// (8 channels) of each of the 8 tokens 8g..8g+7, transposes the 8x8 block in
-// registers and stores 16 bytes (8 tokens) of each of its 8 channels, so each
-// load instruction reads 8 whole 128-byte lines (8 tokens, 64 channels) and
-// each store writes 8 (8 channels, 64 tokens).  Tokens past the end are
-// neither read nor written; a row's last partial 8-token group is stored
-// element by element, so row padding is never touched.
+// 128 channels (two 64-channel blocks; one when D = 64 or for the last block
+// of an odd count) of one head: lane (c = lane % 8, g = lane / 8) loads
+// 16 bytes (8 channels) of each block of each of the 8 tokens 8g..8g+7,
+// transposes each 8x8 block in registers and stores 16 bytes (8 tokens) of
+// each of its channels, so each load instruction reads 8 whole 128-byte lines
+// (8 tokens, 64 channels) and each store writes 8 (8 channels, 64 tokens).
+// Tokens past the end are neither read nor written; a row's last partial
+// 8-token group is stored element by element, so row padding is never touched.
+// A wave takes both channel blocks of its tokens, so a token's 256 bytes of
+// one head are read together: at the Cosmos share the V part ran at 62 % of
+// HBM against 57 % with one block per wave (whole relayout 71.7 % against
+// 69.4 %; Wan's share 72.2 % against 71.4 %).  Clusters of 2 or 4 heads in
+// consecutive workgroups, heads fastest, and plain (cached) loads or stores
+// measured level or slower.
 constexpr int kTokWavesPerBlock = 4;
+
+// units of work: 64-token blocks x pairs of 64-channel blocks, per head
+__host__ __device__ inline int64_t tok_units(int64_t n_tensors, int64_t B, int64_t H_loc, int64_t S, int64_t D) {
+  return n_tensors * B * H_loc * (((S + 63) / 64 + 3) / 4 * 4) * ((D / 64 + 1) / 2);
+}
 
 __device__ __attribute__((always_inline)) void tok_body(const RelayoutArgs& a, int n_units, int block) {
   const int lane = threadIdx.x & 63;
@@ -130,53 +142,59 @@ __device__ __attribute__((always_inline)) void tok_body(const RelayoutArgs& a, i
   const int S = a.P * a.S_loc;
   const int n_tblk = (S + 63) / 64;
   const int n_dh = a.D / 64;
-  // unit = ((((t * B + b) * H_loc + j) * n_dh + dh) * n_tblk4 + tb4) * 4 + tl:
+  const int n_dp = (n_dh + 1) / 2;
+  // unit = ((((t * B + b) * H_loc + j) * n_dp + dp) * n_tblk4 + tb4) * 4 + tl:
   // the 4 waves of a workgroup take 4 consecutive 64-token blocks of one
-  // (head, channel half), so each of its channel rows gets 512 contiguous
-  // bytes (0.9 % faster than 2 token blocks x 2 channel halves at the Cosmos
-  // share, 0.3 % at Wan's; heads fastest, two token blocks per wave, or the
-  // channel halves in adjacent workgroups measured slower)
+  // (head, channel-block pair), so each of its channel rows gets 512
+  // contiguous bytes (0.9 % faster than 2 token blocks x 2 channel blocks)
   const int n_tblk4 = (n_tblk + 3) / 4;
   int rest = unit;
   const int tl = rest % 4; rest /= 4;
   const int tb4 = rest % n_tblk4; rest /= n_tblk4;
-  const int dh = rest % n_dh; rest /= n_dh;
+  const int dp = rest % n_dp; rest /= n_dp;
   const int j = rest % a.H_loc; rest /= a.H_loc;
   const int b = rest % a.B;
   const int t = rest / a.B;
   const int tb = tb4 * 4 + tl;
   if (tb >= n_tblk) return;
+  const int nb = min(2, n_dh - 2 * dp);  // channel blocks of this unit: 1 or 2 (uniform)
   const int c = lane & 7, g = lane >> 3;
   const int tok0 = tb * 64 + 8 * g;
 
-  u32x4 x[8];
+  u32x4 x[2][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int tok = tok0 + k;
-    x[k] = (u32x4){0u, 0u, 0u, 0u};
+    x[0][k] = (u32x4){0u, 0u, 0u, 0u};
+    x[1][k] = (u32x4){0u, 0u, 0u, 0u};
     if (tok < S) {
       const int p = tok / a.S_loc, s = tok - p * a.S_loc;
       const uint16_t* sp = a.src[t][p] + (int64_t)b * a.src_sb[t][p] + (int64_t)s * a.src_ss[t][p] +
-                           (int64_t)(a.rank * a.H_loc + j) * a.src_sh[t][p] + 64 * dh + 8 * c;
-      x[k] = __builtin_nontemporal_load((const u32x4*)sp);
+                           (int64_t)(a.rank * a.H_loc + j) * a.src_sh[t][p] + 128 * dp + 8 * c;
+      x[0][k] = __builtin_nontemporal_load((const u32x4*)sp);
+      if (nb == 2) x[1][k] = __builtin_nontemporal_load((const u32x4*)(sp + 64));
     }
   }
-  uint16_t* dp = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)j * a.dst_sh[t] +
-                 (int64_t)(64 * dh + 8 * c) * a.dst_sd[t] + tok0;
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    // tokens 2i, 2i+1 of channel 8c + dd: the 16-bit halves dd%2 of dword dd/2
-    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 y;
+  for (int h = 0; h < 2; ++h) {
+    if (h >= nb) break;
+    uint16_t* dp_ = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)j * a.dst_sh[t] +
+                    (int64_t)(128 * dp + 64 * h + 8 * c) * a.dst_sd[t] + tok0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_perm(x[2 * i + 1][dd >> 1], x[2 * i][dd >> 1], sel);
-    uint16_t* row = dp + (int64_t)dd * a.dst_sd[t];
-    if (tok0 + 8 <= S) {
-      __builtin_nontemporal_store(y, (u32x4*)row);
-    } else if (tok0 < S) {
+    for (int dd = 0; dd < 8; ++dd) {
+      // tokens 2i, 2i+1 of channel 8c + dd: the 16-bit halves dd%2 of dword dd/2
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 y;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (tok0 + e < S) row[e] = (uint16_t)(y[e >> 1] >> (16 * (e & 1)));
+      for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_perm(x[h][2 * i + 1][dd >> 1], x[h][2 * i][dd >> 1], sel);
+      uint16_t* row = dp_ + (int64_t)dd * a.dst_sd[t];
+      if (tok0 + 8 <= S) {
+        __builtin_nontemporal_store(y, (u32x4*)row);
+      } else if (tok0 < S) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (tok0 + e < S) row[e] = (uint16_t)(y[e >> 1] >> (16 * (e & 1)));
+      }
     }
   }
 }
@@ -201,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) relayout_both_kernel(const RelayoutA
 hipError_t launch_relayout_both(const RelayoutArgs& a, const RelayoutArgs& at, hipStream_t stream) {
   const int64_t n_runs = relayout_runs(a);
   const int64_t S = (int64_t)at.P * at.S_loc;
-  const int64_t n_units = (int64_t)at.n_tensors * at.B * at.H_loc * (((S + 63) / 64 + 3) / 4 * 4) * (at.D / 64);
+  const int64_t n_units = tok_units(at.n_tensors, at.B, at.H_loc, S, at.D);
   if (n_runs > 0x7fffffff || n_units > 0x7fffffff || at.D % 64 != 0 || a.inverse || at.inverse)
     return hipErrorInvalidValue;
   const int64_t n_tok = (n_units + kTokWavesPerBlock - 1) / kTokWavesPerBlock;
@@ -214,7 +232,7 @@ hipError_t launch_relayout_both(const RelayoutArgs& a, const RelayoutArgs& at, h
 
 hipError_t launch_relayout_tok(const RelayoutArgs& a, hipStream_t stream) {
   const int64_t S = (int64_t)a.P * a.S_loc;
-  const int64_t n_units = (int64_t)a.n_tensors * a.B * a.H_loc * (((S + 63) / 64 + 3) / 4 * 4) * (a.D / 64);
+  const int64_t n_units = tok_units(a.n_tensors, a.B, a.H_loc, S, a.D);
   if (n_units == 0) return hipSuccess;
   if (n_units > 0x7fffffff || a.D % 64 != 0 || a.inverse) return hipErrorInvalidValue;
   const int64_t blocks = (n_units + kTokWavesPerBlock - 1) / kTokWavesPerBlock;

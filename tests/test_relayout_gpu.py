@@ -127,7 +127,8 @@ def test_inverse_strided_views_and_guard_bands():
     assert (bb[:, :, -1] == sentinel).all()
 
 
-@pytest.mark.parametrize("P,S_loc,D", [(1, 37, 128), (4, 25, 128), (2, 64, 64), (4, 1, 64), (1, 300, 128)])
+@pytest.mark.parametrize("P,S_loc,D", [(1, 37, 128), (4, 25, 128), (2, 64, 64), (4, 1, 64), (1, 300, 128),
+                                         (2, 40, 192), (1, 70, 256)])
 def test_token_major_destination(P, S_loc, D):
     note(f"relayout into a token-contiguous V: P={P} S_loc={S_loc} D={D}")
     t = torch()
