@@ -16,11 +16,12 @@
 // contiguous elements one token contributes to one tensor from one rank's
 // head slice (or one head's D elements when a view's head slices are not
 // contiguous).  Each wave copies whole runs with 16-byte loads and stores; all
-// loads of a run are issued before its stores.  The forward copy touches every
-// byte once, so its loads and stores are non-temporal (6-8 % faster at the
-// LTX-2 and Wan shares' sizes).  The inverse copy reads an attention output
-// that was just written and is partly still cached, so it keeps plain loads and
-// stores (non-temporal ones made it 6 % slower).  Run indices are wave-uniform,
+// loads of a run are issued before its stores.  Every byte is touched once, so
+// loads and stores are non-temporal: the forward copy 6-8 % faster at the
+// LTX-2 and Wan shares' sizes; the inverse 10 % faster on its own (Wan shard,
+// 69 -> 76 % of HBM) and 3.5 % faster right after the attention that wrote its
+// source at the Cosmos share (74.6 -> 77.2 %), 1.5 % slower there at Wan's
+// (76.3 -> 75.1 %).  Run indices are wave-uniform,
 // so the per-run address arithmetic (tensor, shard, token) stays in scalar
 // registers, in 32 bits (the host keeps the run count at or below 2^30, so a
 // wave's run index plus the grid stride cannot overflow).  Runs are numbered so
@@ -89,16 +90,14 @@ __device__ __attribute__((always_inline)) void copy_body(const RelayoutArgs& a, 
         const int v = v0 + u * 64 + lane;
         if (v < vpr) {
           const u32x4* src = (const u32x4*)(sp + 8 * v);
-          buf[u] = kInverse ? *src : __builtin_nontemporal_load(src);
+          buf[u] = __builtin_nontemporal_load(src);
         }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int v = v0 + u * 64 + lane;
         if (v < vpr) {
-          u32x4* dst = (u32x4*)(dp + 8 * v);
-          if (kInverse) *dst = buf[u];
-          else __builtin_nontemporal_store(buf[u], dst);
+          __builtin_nontemporal_store(buf[u], (u32x4*)(dp + 8 * v));
         }
       }
     }
