@@ -677,7 +677,7 @@ def main():
     flops_per_launch = float(np.mean(pipe.attn_flops_per_launch))
     kernels = {"attn_fwd": rate_entry(dur["attn_fwd"], flops_per_launch, "flop", peak, args.warmup,
                                       launches_per_step=len(pipe.bounds))}
-    for key, nbytes, extra in (("cast_fp8", getattr(pipe, "cast_bytes", 0), {"launches": 3}),
+    for key, nbytes, extra in (("cast_fp8", getattr(pipe, "cast_bytes", 0), {"launches": 4}),
                                ("relayout", pipe.relayout_bytes, {}), ("attn_merge", pipe.merge_bytes, {}),
                                ("relayout_inv", pipe.inverse_bytes, {})):
         if key in dur:
