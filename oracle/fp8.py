@@ -17,6 +17,11 @@ Readings where the pages are silent (also in the design notes):
   with the product rounded to float32 and the code rounded to nearest, ties
   to even; a head that is all zero uses the factor 1 (its codes are 0).
   Dequantised value: decode(code) * (amax / 448) in float32 arithmetic.
+* For Q the stored amax is a scale amax in [amax_q, 2 amax_q): the smallest
+  one at least amax_q for which the logit factor of the default softmax
+  scale, log2(e) / sqrt(128) * (amax_q' / 448) * (amax_k / 448), is a power
+  of two (``q_scale_amax``); Q is coded with it.  The attention kernel can
+  then apply that factor exactly on the matrix cores.
 * FP8 attention computes the attention of the dequantised inputs: its
   definition is ``attention`` applied to them.
 """
@@ -74,6 +79,32 @@ def head_amax(x) -> np.ndarray:
     return v.max(axis=(1, 3)) if v.shape[1] > 0 else np.zeros((v.shape[0], v.shape[2]))
 
 
+# log2(e) / sqrt(128) in float32: the default logit factor of the attention
+# (the softmax scale 1 / sqrt(D) for D = 128, times log2 e, rounded to float32)
+SCALE_LOG2_D128 = np.float32(float(np.float32(1.0 / np.sqrt(128.0))) * 1.4426950408889634074)
+
+
+def q_scale_amax(amax_q, amax_k) -> np.ndarray:
+    """Q's scale amax per (batch, head), in float32 arithmetic step by step:
+    base = SCALE_LOG2_D128 * (amax_k / 448), t = base * (amax_q / 448), e the
+    smallest integer with 2^e >= t, result (2^e / base) * 448 (from 2^(e+1)
+    if that falls below amax_q).  Heads with amax_q or amax_k zero, or a
+    result that is not finite, keep amax_q."""
+    aq = np.asarray(amax_q, dtype=np.float32)
+    ak = np.asarray(amax_k, dtype=np.float32)
+    c448 = np.float32(E4M3_MAX)
+    base = (SCALE_LOG2_D128 * (ak / c448).astype(np.float32)).astype(np.float32)
+    t = (base * (aq / c448).astype(np.float32)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        m, ex = np.frexp(t)                           # t = m 2^ex, m in [0.5, 1)
+        e = np.where(m == np.float32(0.5), ex - 1, ex)
+        r = ((np.ldexp(np.float32(1.0), e).astype(np.float32) / base).astype(np.float32) * c448).astype(np.float32)
+        r2 = ((np.ldexp(np.float32(1.0), e + 1).astype(np.float32) / base).astype(np.float32) * c448).astype(np.float32)
+    r = np.where(r < aq, r2, r)
+    keep = ~(aq > 0) | ~(ak > 0) | ~np.isfinite(r)
+    return np.where(keep, aq, r).astype(np.float32)
+
+
 def quantize(x, amax: np.ndarray) -> np.ndarray:
     """E4M3 codes of x [B, S, H, D] with the per-(batch, head) factor
     448 / amax, computed in float32 as the scale rule states."""
@@ -88,8 +119,9 @@ def quantize(x, amax: np.ndarray) -> np.ndarray:
 
 def cast_qkv(q, k, v):
     """The single FP8 cast pass over Q, K, V: codes for each tensor and the
-    amax array [3, B, H] (q, k, v)."""
+    amax array [3, B, H] (q's entry the scale amax of ``q_scale_amax``, k, v)."""
     amax = np.stack([head_amax(q), head_amax(k), head_amax(v)]).astype(np.float32)
+    amax[0] = q_scale_amax(amax[0], amax[1])
     return quantize(q, amax[0]), quantize(k, amax[1]), quantize(v, amax[2]), amax
 
 

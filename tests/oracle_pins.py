@@ -509,7 +509,8 @@ def pin_e4m3_rounding():
 
 def pin_fp8_cast():
     """The cast: the largest magnitude of each (tensor, batch, head) codes to
-    +-448 exactly; an all-zero head codes to zeros; values already on the
+    +-448 exactly (for Q, whose scale amax may be up to twice its amax, to
+    at least 224); an all-zero head codes to zeros; values already on the
     FP8 grid of their head's scale are reproduced exactly; every dequantised
     value is within half an FP8 ulp (plus the subnormal step) of the input."""
     from oracle import fp8
@@ -520,7 +521,7 @@ def pin_fp8_cast():
     k[1, :, 2, :] = 0                                           # an all-zero head
     q8, k8, v8, amax = fp8.cast_qkv(q, k, v)
     assert amax.shape == (3, B, H)
-    for x, c, a in ((q, q8, amax[0]), (k, k8, amax[1]), (v, v8, amax[2])):
+    for t, (x, c, a) in enumerate(((q, q8, amax[0]), (k, k8, amax[1]), (v, v8, amax[2]))):
         xv = _dec(x)
         for b in range(B):
             for h in range(H):
@@ -528,7 +529,10 @@ def pin_fp8_cast():
                     assert np.all(c[b, :, h] & 0x7F == 0)
                     continue
                 i = np.unravel_index(np.argmax(np.abs(xv[b, :, h])), xv[b, :, h].shape)
-                assert (c[b, :, h][i] & 0x7F) == 0x7E
+                if t == 0:
+                    assert 224.0 <= fp8.e4m3_decode(c[b, :, h][i] & 0x7F) <= 448.0
+                else:
+                    assert (c[b, :, h][i] & 0x7F) == 0x7E
         deq = fp8.dequantize(c, a)
         step = (np.asarray(a, np.float64) / 448.0)[:, None, :, None]
         assert np.all(np.abs(deq - xv) <= np.abs(xv) * 2.0 ** -4 + step * 2.0 ** -9 * 1.01)
@@ -537,6 +541,36 @@ def pin_fp8_cast():
     codes[0, 3, 0, 5] = 0x7E                                    # amax = 448 -> factor 1
     xb = synth.f32_to_bf16_bits(fp8.e4m3_decode(codes).astype(np.float32))
     assert np.array_equal(fp8.quantize(xb, fp8.head_amax(xb)), codes)
+
+
+def pin_fp8_q_scale():
+    """Q's scale amax: at least amax_q and below 2 amax_q, and with it the
+    default logit factor log2(e) / sqrt(128) * (amax_q' / 448) * (amax_k / 448)
+    is a power of two (checked in float64, to 2^-20); heads whose amax_q or
+    amax_k is zero keep amax_q; the cast stores it as Q's amax."""
+    from oracle import fp8
+    g = np.random.Generator(np.random.PCG64(56))
+    aq = np.exp(g.uniform(-25.0, 25.0, size=4000)).astype(np.float32)
+    ak = np.exp(g.uniform(-25.0, 25.0, size=4000)).astype(np.float32)
+    aq[:8] = [1.0, 448.0, 2.0 ** -10, 3.0, 1.0, 1.5, 7.0, 100.0]
+    ak[:8] = [1.0, 448.0, 2.0 ** 10, 3.0, 448.0, 0.75, 7.0, 0.01]
+    r = fp8.q_scale_amax(aq, ak).astype(np.float64)
+    a64, k64 = aq.astype(np.float64), ak.astype(np.float64)
+    assert np.all(r >= a64) and np.all(r < 2.0 * a64 * (1.0 + 2.0 ** -20))
+    c = (np.log2(np.e) / np.sqrt(128.0)) * (r / 448.0) * (k64 / 448.0)
+    lg = np.log2(c)
+    assert np.all(np.abs(lg - np.round(lg)) < 2.0 ** -20 / np.log(2.0))
+    z = fp8.q_scale_amax(np.array([0.0, 5.0, 0.0], np.float32), np.array([3.0, 0.0, 0.0], np.float32))
+    assert np.array_equal(z, np.array([0.0, 5.0, 0.0], np.float32))
+    B, S, H, D = 1, 20, 3, 64
+    q, k, v = _rand((B, S, H, D), 57), _rand((B, S, H, D), 58), _rand((B, S, H, D), 59)
+    _, _, _, amax = fp8.cast_qkv(q, k, v)
+    aq2, ak2 = fp8.head_amax(q).astype(np.float64), fp8.head_amax(k).astype(np.float64)
+    a0 = amax[0].astype(np.float64)
+    assert np.all(a0 >= aq2) and np.all(a0 < 2.0 * aq2 * (1.0 + 2.0 ** -20))
+    lg = np.log2((np.log2(np.e) / np.sqrt(128.0)) * (a0 / 448.0) * (ak2 / 448.0))
+    assert np.all(np.abs(lg - np.round(lg)) < 2.0 ** -20 / np.log(2.0))
+    assert np.array_equal(amax[1], fp8.head_amax(k).astype(np.float32))
 
 
 def pin_fp8_attention():
@@ -566,5 +600,5 @@ def pin_fp8_attention():
     assert np.allclose(o_r, O[0, rows, 1], rtol=0, atol=1e-12) and np.allclose(l_r, L[0, 1, rows], rtol=0, atol=1e-12)
 
 
-FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_attention]
+FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_q_scale, pin_fp8_attention]
 ALL_PINS = ALL_PINS + FP8_PINS

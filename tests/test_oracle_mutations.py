@@ -285,9 +285,36 @@ def _dequant_no_scale(codes, amax):
     return _orig_decode(codes)
 
 
+_orig_qscale = _fp8.q_scale_amax
+
+
+def _qscale_identity(amax_q, amax_k):
+    return np.asarray(amax_q, dtype=np.float32)
+
+
+def _qscale_no_log2e(amax_q, amax_k):
+    # the softmax scale without log2(e): a power of two in natural-log units
+    return _orig_qscale(amax_q, np.asarray(amax_k, np.float32) / np.float32(np.log2(np.e)))
+
+
+def _qscale_uses_q(amax_q, amax_k):
+    return _orig_qscale(amax_q, amax_q)
+
+
+def _qscale_power_too_low(amax_q, amax_k):
+    return (_orig_qscale(amax_q, amax_k) * np.float32(0.5)).astype(np.float32)
+
+
+def _qscale_power_too_high(amax_q, amax_k):
+    r = _orig_qscale(amax_q, amax_k)
+    return np.where(np.asarray(amax_q) > 0, r * np.float32(2.0), r).astype(np.float32)
+
+
 FP8_MUTANTS = [("e4m3_encode", _encode_ties_away), ("e4m3_encode", _encode_truncate),
                ("e4m3_decode", _decode_fnuz_bias), ("head_amax", _amax_per_tensor),
-               ("dequantize", _dequant_no_scale)]
+               ("dequantize", _dequant_no_scale), ("q_scale_amax", _qscale_identity),
+               ("q_scale_amax", _qscale_no_log2e), ("q_scale_amax", _qscale_uses_q),
+               ("q_scale_amax", _qscale_power_too_low), ("q_scale_amax", _qscale_power_too_high)]
 
 
 @pytest.mark.parametrize("name,mutant", FP8_MUTANTS, ids=lambda f: getattr(f, "__name__", str(f)))
