@@ -205,14 +205,23 @@ lsd_status lsd_attn_merge(int n, const lsd_view4* o_parts, const float* const* l
  *         (stride[1] = 1), stride[3] = row pitch of one (b, h, d) row, at
  *         least S rounded up to 64: the cast also writes zero codes for the
  *         tokens S .. that bound (each row must be allocated that far)
- *   amax  float32 [3, B, H]: max |x| over tokens and channels of each
- *         (tensor, batch, head), written
+ *   amax  float32 [3, B, H]: per (tensor, batch, head) the scale amax the
+ *         codes use, written: for K and V max |x| over tokens and channels;
+ *         for Q the smallest value amax_q' >= max |q| for which
+ *         log2(e)/sqrt(128) * (amax_q'/448) * (amax_k/448) is a power of two
+ *         (float32 steps: base = log2(e)/sqrt(128) * (amax_k/448),
+ *         t = base * (amax_q/448), 2^e the smallest power of two >= t,
+ *         amax_q' = (2^e / base) * 448, from 2^(e+1) if that falls below
+ *         amax_q; it lies in [amax_q, 2 amax_q)); a zero amax_q or amax_k,
+ *         or a result that is not finite, keeps amax_q
  *
  * code = E4M3(x * (448 / amax)): the product rounded to float32, the code to
  * nearest, ties to even (OCP E4M3: largest finite 448); a head whose amax is
- * 0 uses factor 1.  The dequantised value is code * (amax / 448).  All other
+ * 0 uses factor 1.  The dequantised value is code * (amax / 448).  The Q scale
+ * makes lsd_attn_fwd_fp8's logit factor at the default softmax scale an exact
+ * power of two, which that kernel applies on the matrix cores.  All other
  * byte strides and pointers must be multiples of 16.  Deterministic (the amax
- * reduction takes maxima, which do not depend on order).  Three launches on
+ * reduction takes maxima, which do not depend on order).  Four launches on
  * `stream`.
  */
 lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream);
@@ -233,13 +242,17 @@ lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* a
  *            codes, up to S_kv rounded up to 64 tokens from the view's start
  *            (the cast's padded rows satisfy this for views that start at a
  *            multiple of 64 tokens), and stride[3] must be at least that
- *   q_amax, k_amax, v_amax  float32 [B, H]: the amax of each tensor
+ *   q_amax, k_amax, v_amax  float32 [B, H]: the scale amax of each tensor
+ *            (as lsd_cast_qkv_fp8 writes them; any positive values work)
  *   o        bf16 (B, S_q, H, D), written;  lse  float32 [B, H, S_q] or NULL
  *
  * D = 128 only.  The softmax weights are rounded to E4M3 for the PV product
  * (the row sums stay float32), so O carries an error of up to 2^-4 of
  * sum_j p_j |v_j| / l (see the design notes for the full bound); LSE is as
- * exact as in lsd_attn_fwd.  S_kv == 0 gives O = 0, LSE = -inf.
+ * exact as in lsd_attn_fwd.  When scale * log2(e) * (q_amax/448) *
+ * (k_amax/448) is within 2^-20 of a power of two, that power of two is used
+ * as the logit factor (a relative change of at most 2^-20).  S_kv == 0 gives
+ * O = 0, LSE = -inf.
  */
 lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
                             const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,

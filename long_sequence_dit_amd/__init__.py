@@ -256,7 +256,9 @@ def fp8_buffers(B, S, H, D=128, device="cuda"):
 def cast_qkv_fp8(q, k, v, out=None):
     """One FP8 (E4M3) cast of Q, K, V (bf16 (B, S, H, D) views) with one scale
     per (tensor, batch, head).  Returns (q8, k8, v8, amax): v8 is a (B, S, H, D)
-    view of V stored transposed; amax[t] is tensor t's per-(b, h) amax."""
+    view of V stored transposed; amax[t] is tensor t's per-(b, h) scale amax
+    (K, V: max |x|; Q: the power-of-two-adjusted value in [amax_q, 2 amax_q)
+    described in include/lsd.h)."""
     B, S, H, D = q.shape
     if out is None:
         out = fp8_buffers(B, S, H, D, q.device)

@@ -29,6 +29,15 @@
 // * The dequantisation factors fold into the softmax scale (s_q s_k) and the
 //   final normalisation (s_v / l); weights are <= 2^8 (lazy rescaling), well
 //   inside E4M3's range of 448.
+// * When the logit factor c = scale log2(e) s_q s_k is a power of two (within
+//   2^-20, as the cast's scale amax of Q makes the default one), the QK^T
+//   products apply it exactly through the instruction's E8M0 block scales,
+//   so scores arrive in log2 units.  The reference max m is then kept an
+//   integer, and while |m| <= 100 a weight is exp2 of the score alone: the
+//   E4M3 conversion divides by 2^m (its scale operand) and the tile's sum is
+//   multiplied by 2^-m once, one VALU instruction per score fewer than
+//   exp2(s c - m).  The first tile, |m| > 100 and the tiles that raise m use
+//   that form.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -92,6 +101,18 @@ __device__ inline float partner_sum(float x) {
 __device__ inline f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// with E8M0 block scales (127 = 2^0) on both operands
+__device__ inline f32x16 mfma_fp8_scaled(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+// four float32 values divided by 2^(exponent of scale) -> four E4M3 codes
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack4_fp8_scaled(uint32_t old, float a, float b, float c, float d, float scale) {
+  s16x2 v = __builtin_bit_cast(s16x2, old);
+  v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, a, b, scale, false);
+  v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, c, d, scale, true);
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // LDS row of key kk (0..63) in a K tile: within each 32-key block, key
 // 16 hh + r sits in row 8 (r / 4) + 4 hh + r % 4.
@@ -128,6 +149,17 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   const float s_k = a.k_amax[b * a.H + h] / 448.0f;
   const float s_v = a.v_amax[b * a.H + h] / 448.0f;
   const float c = a.scale_log2 * s_q * s_k;
+  // power-of-two logit factor 2^pe: E8M0 scales 127 + e1 and 127 + e2
+  int cex;
+  const float cm = frexpf(c, &cex);  // c = cm 2^cex, cm in [0.5, 1)
+  int pe = 0;
+  bool pow2 = false;
+  if (fabsf(cm - 0.5f) <= 0x1p-21f) { pow2 = true; pe = cex - 1; }
+  else if (fabsf(cm - 1.0f) <= 0x1p-20f) { pow2 = true; pe = cex; }
+  pow2 = pow2 && pe >= -254 && pe <= 254;
+  const int qk_sa = pow2 ? 127 + pe / 2 : 127;
+  const int qk_sb = pow2 ? 127 + (pe - pe / 2) : 127;
+  const float cs = pow2 ? 1.0f : c;  // factor still to apply to a score
 
   // ---- Q rows of this wave: 32 codes per lane per 64-channel step.
   const int qrow = qt * kBlockM + wave * 32 + l32;
@@ -184,7 +216,8 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // an integer on the power-of-two path once set
+  float m_pow = 0.0f, m_inv = 0.0f, m_lim = 0.0f;  // 2^m, 2^-m, 2^(m+8) for the power-of-two path
   float l_run = 0.0f;
   f32x16 sacc[2];
   uint32_t pk[8] = {};  // this tile's weights as E4M3, in PV operand order
@@ -205,13 +238,30 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 0], c, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
-      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 2], c, neg_m));
-      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 3], c, neg_m));
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 0], cs, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], cs, neg_m));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 2], cs, neg_m));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 3], cs, neg_m));
       lt0 = (w == 0) ? p0 + p2 : lt0 + (p0 + p2);  // no 0 + x: the first pair starts the sum
       lt1 = (w == 0) ? p1 + p3 : lt1 + (p1 + p3);
       pk[w] = pack4_fp8_over(pk[w], p0, p1, p2, p3);  // the previous tile's codes are dead
+    }
+    return lt0 + lt1;
+  };
+  // The power-of-two path's form: p = exp2(s) (scores in log2 units), codes
+  // of p / 2^m; returns the tile's sum of p (not yet divided by 2^m).
+  auto exps_pow = [&]() __attribute__((always_inline)) -> float {
+    float lt0 = 0.0f, lt1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r = 4 * (w & 3);
+      const float p0 = __builtin_amdgcn_exp2f(sacc[kb][r + 0]);
+      const float p1 = __builtin_amdgcn_exp2f(sacc[kb][r + 1]);
+      const float p2 = __builtin_amdgcn_exp2f(sacc[kb][r + 2]);
+      const float p3 = __builtin_amdgcn_exp2f(sacc[kb][r + 3]);
+      lt0 = (w == 0) ? p0 + p2 : lt0 + (p0 + p2);
+      lt1 = (w == 0) ? p1 + p3 : lt1 + (p1 + p3);
+      pk[w] = pack4_fp8_scaled(pk[w], p0, p1, p2, p3, m_pow);
     }
     return lt0 + lt1;
   };
@@ -222,8 +272,20 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   // the row max, rescales and forms them again: the same result as always
   // taking the max, with about 20 fewer instructions per tile.
   auto softmax = [&]() __attribute__((always_inline)) {
-    float lt = exps();
-    if (__any(!(lt <= 256.0f))) {
+    float lt;
+    bool slow;
+    // power-of-two path with |m| <= 100 (wave-uniform): exp2(s) cannot
+    // overflow while weights stay <= 2^8 relative to m, nor underflow for
+    // the row's larger weights
+    if (pow2 && __all(m_run >= -100.0f && m_run <= 100.0f)) {
+      lt = exps_pow();
+      slow = __any(!(lt <= m_lim));
+      lt *= m_inv;
+    } else {
+      lt = exps();
+      slow = __any(!(lt <= 256.0f));
+    }
+    if (slow) {
       float mx0 = sacc[0][0], mx1 = sacc[1][0];
 #pragma unroll
       for (int r = 1; r < 15; r += 2) {
@@ -231,17 +293,26 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
         mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
       }
       float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
-      mx = partner_max(mx) * c;
+      mx = partner_max(mx) * cs;
       const float m_new = vmax(m_run, mx);
       const bool need = m_new > m_run + kRescaleThreshold;
       if (__any(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        m_run = need ? m_new : m_run;
+        // the power-of-two path keeps m an integer (weights relative to it
+        // stay <= 2^8), so 2^m, 2^-m and every rescale factor are exact
+        const float m_set = pow2 ? ceilf(m_new) : m_new;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_set) : 1.0f;
+        m_run = need ? m_set : m_run;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        if (pow2) {
+          const int mi = (int)fmaxf(fminf(m_run, 120.0f), -120.0f);
+          m_pow = ldexpf(1.0f, mi);
+          m_inv = ldexpf(1.0f, -mi);
+          m_lim = ldexpf(1.0f, mi + 8);
+        }
       }
       lt = exps();
     }
@@ -279,7 +350,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
         oacc[i] = mfma_fp8(cur, pb, oacc[i]);
       } else {
         const int j = i - 4, kb = j >> 1, s = j & 1;
-        sacc[kb] = mfma_fp8(cur, qreg[s], s == 0 ? (f32x16){} : sacc[kb]);
+        sacc[kb] = mfma_fp8_scaled(cur, qreg[s], s == 0 ? (f32x16){} : sacc[kb], qk_sa, qk_sb);
       }
       if (i == 1) store_k(t + 2);
       if (i == 2) store_v(t + 1);
@@ -311,7 +382,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
         const u32x4 lo = *(const u32x4*)p;
         const u32x4 hi = *(const u32x4*)(p + 16);
         const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sacc[kb] = mfma_fp8(kf, qreg[s], sacc[kb]);
+        sacc[kb] = mfma_fp8_scaled(kf, qreg[s], sacc[kb], qk_sa, qk_sb);
       }
     }
   }

@@ -8,6 +8,11 @@
 // Per (tensor t, batch b, head h): amax = max |x| over tokens and channels;
 // code = E4M3(x * (448 / amax)) with the product rounded to float32 and the
 // code rounded to nearest even (v_cvt_pk_fp8_f32); amax == 0 uses factor 1.
+// Q is coded with a scale amax instead (stored in place of its amax): the
+// smallest value in [amax_q, 2 amax_q) for which the default logit factor
+// log2(e)/sqrt(128) * (amax_q'/448) * (amax_k/448) is a power of two, so
+// that the attention can apply it exactly through the FP8 matrix cores'
+// block scales (q_scale_amax; heads with a zero amax keep amax_q).
 // Q and K keep their (B, S, H, D) layout; V is written transposed, keys
 // contiguous per (b, h, d), which is the operand layout of the PV product.
 //
@@ -91,6 +96,32 @@ __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs)
 
 __device__ inline float inv_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 1.0f; }
 
+// log2(e) / sqrt(128) in float32 (0x3e0293ee): the attention's default
+// logit factor (softmax scale 1/sqrt(D) for D = 128, times log2 e)
+constexpr float kScaleLog2D128 = 0x1.0527dcp-3f;
+
+// Q's scale amax, in float32 step by step: base = kScaleLog2D128 *
+// (amax_k / 448), t = base * (amax_q / 448), e the smallest integer with
+// 2^e >= t, result (2^e / base) * 448, from 2^(e+1) if that falls below
+// amax_q; a zero amax, or a result that is not finite, keeps amax_q.
+__device__ inline float q_scale_amax(float aq, float ak) {
+  if (!(aq > 0.0f) || !(ak > 0.0f)) return aq;
+  const float base = kScaleLog2D128 * (ak / 448.0f);
+  const float t = base * (aq / 448.0f);
+  int ex;
+  const float m = frexpf(t, &ex);  // t = m 2^ex, m in [0.5, 1)
+  const int e = (m == 0.5f) ? ex - 1 : ex;
+  float r = (ldexpf(1.0f, e) / base) * 448.0f;
+  if (r < aq) r = (ldexpf(1.0f, e + 1) / base) * 448.0f;
+  return (r <= 3.402823466e38f) ? r : aq;
+}
+
+// the factor that codes tensor t of (b, h): 448 / amax, Q's from its scale amax
+__device__ inline float code_factor(const CastArgs& a, int t, int64_t bh) {
+  const float am = a.amax[(int64_t)t * a.B * a.H + bh];
+  return inv_scale(t == 0 ? q_scale_amax(am, a.amax[(int64_t)a.B * a.H + bh]) : am);
+}
+
 // Per-head Q and K pass (any strides; contiguous tensors with contiguous code
 // outputs take the flat pass below): one wave per (t in {0,1}, b, h, 64 tokens), heads fastest so that
 // waves running together read whole token rows; 16-byte bf16 vectors in,
@@ -106,7 +137,7 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
   const int chunk = (int)(rest % n_chunks);
   const int b = (int)((rest / n_chunks) % a.B);
   const int t = (int)(rest / ((int64_t)n_chunks * a.B));
-  const float inv = inv_scale(a.amax[((int64_t)t * a.B + b) * a.H + h]);
+  const float inv = code_factor(a, t, (int64_t)b * a.H + h);
   const uint16_t* src = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t] + 8 * (lane & 15);
   uint8_t* dst = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)h * a.dst_sh[t] + 8 * (lane & 15);
   const int s0 = chunk * kChunk + (lane >> 4);
@@ -149,6 +180,12 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   const float inv = inv_scale(a.amax[((int64_t)2 * a.B + b) * a.H + h]);
   const uint16_t* src = a.src[2] + (int64_t)b * a.src_sb[2] + (int64_t)h * a.src_sh[2];
   const int s0 = chunk * kVTok;
+  // Q's stored amax becomes its scale amax; the Q pass (an earlier launch)
+  // has finished reading it
+  if (chunk == 0 && threadIdx.x == 0) {
+    float* aq = &a.amax[(int64_t)b * a.H + h];
+    *aq = q_scale_amax(*aq, a.amax[((int64_t)a.B + b) * a.H + h]);
+  }
   const int tid = threadIdx.x;
   const int g = tid >> 4;      // token group (0..15)
   const int c = tid & 15;      // channel chunk (0..15)
@@ -262,7 +299,7 @@ __global__ void __launch_bounds__(256) quant_qk_flat_kernel(const CastArgs a, in
   float inv[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u)
-    inv[u] = inv_scale(a.amax[(int64_t)seg * a.H + (int)(((first + 256 * u) / 16) % a.H)]);
+    inv[u] = code_factor(a, t, (int64_t)b * a.H + (int)(((first + 256 * u) / 16) % a.H));
   for (int64_t i0 = first; i0 < n; i0 += stride) {
     u32x4 x[kU];
 #pragma unroll
