@@ -52,7 +52,9 @@
 extern "C" {
 #endif
 
-#define LSD_ABI_VERSION 1
+/* 2: lsd_cast_qkv_fp8 stores Q's scale amax (a power-of-two logit factor)
+ *    in place of Q's plain amax; signatures unchanged from 1. */
+#define LSD_ABI_VERSION 2
 
 typedef enum lsd_status {
   LSD_OK = 0,

@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
             "lsd_abi_version", "lsd_last_error"} <= set(syms)
     for s in syms:
         assert hasattr(L, s), f"{s} declared in lsd.h but not exported by liblsd.so"
-    assert L.lsd_abi_version() == 1
+    assert L.lsd_abi_version() == 2
 
 
 def view(addr, shape, stride=None):
