@@ -389,16 +389,13 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   const float l_tot = partner_sum(l_run);
   const float inv = 1.0f / l_tot;
   constexpr float kLn2 = 0.69314718055994530942f;
-  float osc = inv;  // scale from oacc to the output values
   if constexpr (kAcc) {
     // Merge with the running result of earlier key blocks (exact LSE merge,
     // fp32): with M = max(LSE_acc, LSE_blk) and w = exp(LSE - M),
     //   O_acc <- (w_acc O_acc + w_blk O_blk) / (w_acc + w_blk),
     //   LSE_acc <- M + ln(w_acc + w_blk).
     // LSE_blk is finite (the block has keys), so M is; rows with no history
-    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.  Each lane
-    // reads and writes its row's 16-byte runs of O_acc in the accumulator
-    // layout (channels 32 db + 8 g + 4 hh .. +3).
+    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.
     const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + qrow;
     const float lse_b = (m_run + __log2f(l_tot)) * kLn2;
     const float lse_a = qvalid ? a.lse_acc[lrow] : -INFINITY;
@@ -407,24 +404,56 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     const float wb = expf(lse_b - mx);
     const float rs = 1.0f / (wa + wb);
     const float ca = wa * rs, cb = wb * rs * inv;
-    float* orow = a.o_acc + (((int64_t)b * a.S_q + qrow) * a.H + h) * D + 4 * hh;
-#pragma unroll
-    for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 prev = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (qvalid && wa > 0.0f) prev = *(const f32x4*)(orow + 32 * db + 8 * g);
-        f32x4 nv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          nv[e] = prev[e] * ca + oacc[db][4 * g + e] * cb;
-          oacc[db][4 * g + e] = nv[e];
-        }
-        if (qvalid) *(f32x4*)(orow + 32 * db + 8 * g) = nv;
-      }
     if (hh == 0 && qvalid) a.lse_acc[lrow] = mx + logf(wa + wb);
-    osc = 1.0f;
-    if (a.o == nullptr) return;  // uniform: no bf16 output requested
+    // The block's weighted rows (w_blk O_blk / (w_acc + w_blk)) go through LDS
+    // (the K/V buffers are free once every wave has left the loop), half of D
+    // at a time (a whole fp32 tile does not fit this kernel's LDS), so that
+    // the fp32 running O is read and written in contiguous row pieces (256
+    // bytes at D = 128) rather than 16-byte pieces of 32 rows.  Each wave
+    // uses its own region; a row's history weight w_acc / (w_acc + w_blk)
+    // comes from the lane that holds the row (lane r, r < 32).
+    __syncthreads();
+    constexpr int kW = D / 2;      // columns per pass
+    constexpr int kRowA = kW + 4;  // pitch (floats)
+    static_assert(kWaves * 32 * kRowA * 4 <= (int)sizeof(smem), "fp32 staging fits the stage buffers");
+    float* Aw = (float*)smem + wave * 32 * kRowA;
+    constexpr int kCPR = kW / 4;             // 16-byte chunks per row piece
+    constexpr int kRowsPerPass = 64 / kCPR;  // 4 rows per pass at D = 128, 8 at D = 64
+    const int ch = lane % kCPR;
+    const int row_base = qt * kBlockM + wave * 32;
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+      for (int db = hp * kW / 32; db < (hp + 1) * kW / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 w = {oacc[db][4 * g + 0] * cb, oacc[db][4 * g + 1] * cb, oacc[db][4 * g + 2] * cb,
+                           oacc[db][4 * g + 3] * cb};
+          *(f32x4*)(Aw + l32 * kRowA + 32 * db - hp * kW + 8 * g + 4 * hh) = w;
+        }
+      // (this wave's LDS operations complete in order: the reads below see
+      // the writes above, and the next pass's writes follow these reads)
+#pragma unroll
+      for (int it = 0; it < 32 / kRowsPerPass; ++it) {
+        // the whole wave takes every step, so the lane shuffle reads active lanes
+        const int r = it * kRowsPerPass + lane / kCPR;
+        const float car = __shfl(ca, r);
+        const int row = row_base + r;
+        if (row >= a.S_q) continue;
+        f32x4 nv = *(const f32x4*)(Aw + r * kRowA + 4 * ch);
+        float* gp = a.o_acc + (((int64_t)b * a.S_q + row) * a.H + h) * D + hp * kW + 4 * ch;
+        if (car > 0.0f) {  // history exists (w_acc > 0): O_acc holds data
+          const f32x4 prev = *(const f32x4*)gp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nv[e] = __builtin_fmaf(prev[e], car, nv[e]);
+        }
+        *(f32x4*)gp = nv;
+        if (a.o != nullptr)
+          *(u32x2*)(a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh + hp * kW + 4 * ch) =
+              (u32x2){pack_bf16(nv[0], nv[1]), pack_bf16(nv[2], nv[3])};
+      }
+    }
+    return;
   }
   // Stage this wave's 32 x D output tile through LDS (the K/V buffers are free
   // once every wave has left the loop) so that global stores write whole
@@ -436,11 +465,11 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   for (int db = 0; db < C::kDBlocks; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * osc, oacc[db][4 * g + 1] * osc),
-                 pack_bf16(oacc[db][4 * g + 2] * osc, oacc[db][4 * g + 3] * osc)};
+      u32x2 w = {pack_bf16(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                 pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
       *(u32x2*)(Ow + l32 * kRowO + 32 * db + 8 * g + 4 * hh) = w;
     }
-  if (!kAcc && a.lse != nullptr && hh == 0 && qvalid)
+  if (a.lse != nullptr && hh == 0 && qvalid)
     a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   // rows are written by 64 lanes: lane = (row r in 0..64/CPR-1, 16-B chunk)
   constexpr int kCPR = D / 8;  // 16-byte chunks per row
