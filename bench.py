@@ -480,7 +480,7 @@ def leg_ltx2(fp8=False):
                 "attn_fwd": attn_leg(lambda: lsd.attn_fwd(dq, dk, dvt, o=o, lse=lse), flop)}
     bufs = lsd.fp8_buffers(B, S, H, D)
     cast_bytes = 3 * B * S * H * D * (2 + 2 + 1)
-    cast = hbm_leg(lambda: lsd.cast_qkv_fp8(dq, dk, dv, out=bufs), cast_bytes, launches=3)
+    cast = hbm_leg(lambda: lsd.cast_qkv_fp8(dq, dk, dv, out=bufs), cast_bytes, launches=4)
     q8, k8, v8, amax = bufs
     att = attn_leg(lambda: lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2], o=o, lse=lse), flop,
                    peak=PEAK_FP8_TFLOPS)
