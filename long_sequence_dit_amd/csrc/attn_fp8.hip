@@ -10,8 +10,10 @@
 // Challenge in Video Generation": dense, unmasked attention).
 //
 // The structure follows the bf16 kernel (8 waves, 256 query rows per
-// workgroup, 64-key tiles double-buffered in LDS, the two waves of a SIMD
-// alternating MFMA and softmax phases); the products run on
+// workgroup, key tiles double-buffered in LDS, the two waves of a SIMD
+// alternating MFMA and softmax phases), with 128-key tiles (the FP8 operands
+// leave the registers for them, and each barrier hand-off between the phases
+// then serves twice the keys); the products run on
 // v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 rate).  In that instruction
 // lane l (row or column l % 32) holds 32 codes of the 64-long reduction for
 // lane half l / 32, and only the pairing of A and B matters, so the kernel
@@ -21,8 +23,9 @@
 // * K rows are stored in LDS permuted (row 8 (r/4) + 4 hh + r % 4 of a 32-key
 //   block holds key 16 hh + r), so accumulator register r of lane half hh is
 //   the score of key 16 hh + r: each lane half holds 16 consecutive keys.
-// * PV: O^T = V^T P^T, reduction over the tile's 64 keys; byte j of lane half
-//   hh is key 32 (j / 16) + 16 hh + j % 16.  The softmax weights, converted to
+// * PV: O^T = V^T P^T, reduction over each 64-key half of the tile; byte j of
+//   lane half hh is key 32 (j / 16) + 16 hh + j % 16 of the half (64-key
+//   blocks of 2 x 32 keys).  The softmax weights, converted to
 //   E4M3 in accumulator order, are the B operand as they stand, and the A
 //   operand is two 16-byte pieces of a V^T row (V arrives transposed, keys
 //   contiguous, from the cast).
@@ -57,7 +60,7 @@ constexpr int D = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;       // query rows per workgroup
-constexpr int kBlockN = 64;                // keys per LDS tile
+constexpr int kBlockN = 128;               // keys per LDS tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units; keeps weights <= 2^8
 constexpr int kRowK = D + 16;              // K row pitch (bytes): 16-byte skew per row
 constexpr int kRowV = kBlockN + 16;        // V^T row pitch (bytes)
@@ -118,7 +121,7 @@ __device__ inline uint32_t pack4_fp8_scaled(uint32_t old, float a, float b, floa
 // 16 hh + r sits in row 8 (r / 4) + 4 hh + r % 4.
 __device__ inline int k_lds_row(int kk) {
   const int x = kk & 31;
-  return (kk & 32) + 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3);
+  return (kk & ~31) + 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3);
 }
 
 __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a, int n_qtiles) {
@@ -183,30 +186,47 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   // of 64 tokens, so a tile never leaves its rows.
   const uint8_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const uint8_t* vbase = a.vt + (int64_t)b * a.vt_sb + (int64_t)h * a.vt_sh;
-  const int k_key = tid >> 3, k_ch = tid & 7;
-  const uint32_t k_off = (uint32_t)(k_key * a.k_ss + 16 * k_ch);
-  const int k_dst = k_lds_row(k_key) * kRowK + 16 * k_ch;
-  const int v_d = tid >> 2, v_q = tid & 3;
-  const uint32_t v_off = (uint32_t)(v_d * a.vt_sd + 16 * v_q);
-  const int v_dst = v_d * kRowV + 16 * v_q;
-  const int v_range = (int)((D - 1) * a.vt_sd + kBlockN);
-  u32x4 kst, vst;
+  const int k_key = tid >> 3, k_ch = tid & 7;  // pieces: keys k_key and k_key + 64
+  const uint32_t k_off0 = (uint32_t)(k_key * a.k_ss + 16 * k_ch);
+  const uint32_t k_off1 = (uint32_t)((k_key + 64) * a.k_ss + 16 * k_ch);
+  const int k_dst0 = k_lds_row(k_key) * kRowK + 16 * k_ch;
+  const int k_dst1 = k_lds_row(k_key + 64) * kRowK + 16 * k_ch;
+  const int v_d = tid >> 3, v_q = tid & 7;  // pieces: V^T rows v_d and v_d + 64, keys [16 v_q, +16)
+  const uint32_t v_off0 = (uint32_t)(v_d * a.vt_sd + 16 * v_q);
+  const uint32_t v_off1 = (uint32_t)((v_d + 64) * a.vt_sd + 16 * v_q);
+  const int v_dst0 = v_d * kRowV + 16 * v_q;
+  const int v_dst1 = (v_d + 64) * kRowV + 16 * v_q;
+  const int v_range = (int)((D - 1) * a.vt_sd + kBlockN);  // < 2^31: row pitch < 2^24
+  const uint32_t v_hi_oob = (v_q >= 4) ? 0x80000000u : 0u;  // offsets >= 2^31 lie past the range
+  u32x4 kst0, kst1, vst0, vst1;
   auto load_k = [&](int t) {
     const int64_t rows = (int64_t)skv - (int64_t)t * kBlockN;
     const int64_t any = -(int64_t)(rows > 0);
     const int n = (int)(((min(rows, (int64_t)kBlockN) - 1) * a.k_ss + D) & any);
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)t * kBlockN * a.k_ss), (short)0, n, 0x00020000);
-    kst = __builtin_amdgcn_raw_buffer_load_b128(r, k_off, 0, 0);
+    kst0 = __builtin_amdgcn_raw_buffer_load_b128(r, k_off0, 0, 0);
+    kst1 = __builtin_amdgcn_raw_buffer_load_b128(r, k_off1, 0, 0);
   };
+  // V^T rows are readable to S_kv rounded up to 64 tokens: where a tile's
+  // second 64 keys lie past that, their pieces take an offset beyond the
+  // buffer range and read as zero
   auto load_v = [&](int t) {
     const int n = (t < n_tiles) ? v_range : 0;
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)t * kBlockN), (short)0, n, 0x00020000);
-    vst = __builtin_amdgcn_raw_buffer_load_b128(r, v_off, 0, 0);
+    const uint32_t oob = (t * kBlockN + 64 >= skv) ? v_hi_oob : 0u;  // wave-uniform choice
+    vst0 = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0 | oob, 0, 0);
+    vst1 = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1 | oob, 0, 0);
   };
-  auto store_k = [&](int t) { *(u32x4*)(Ks + (t & 1) * kLdsK + k_dst) = kst; };
-  auto store_v = [&](int t) { *(u32x4*)(Vs + (t & 1) * kLdsV + v_dst) = vst; };
+  auto store_k = [&](int t) {
+    *(u32x4*)(Ks + (t & 1) * kLdsK + k_dst0) = kst0;
+    *(u32x4*)(Ks + (t & 1) * kLdsK + k_dst1) = kst1;
+  };
+  auto store_v = [&](int t) {
+    *(u32x4*)(Vs + (t & 1) * kLdsV + v_dst0) = vst0;
+    *(u32x4*)(Vs + (t & 1) * kLdsV + v_dst1) = vst1;
+  };
   auto lds_barrier = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -219,16 +239,23 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   float m_run = -INFINITY;  // an integer on the power-of-two path once set
   float m_pow = 0.0f, m_inv = 0.0f, m_lim = 0.0f;  // 2^m, 2^-m, 2^(m+8) for the power-of-two path
   float l_run = 0.0f;
-  f32x16 sacc[2];
-  uint32_t pk[8] = {};  // this tile's weights as E4M3, in PV operand order
+  f32x16 sacc[4];
+  uint32_t pk[16] = {};  // this tile's weights as E4M3, in PV operand order (two 64-key halves)
 
   auto mask_tail = [&](int t) {
-    const int kv0 = t * kBlockN;
+    // keys of this lane's scores at or past `lim` (tile-relative) are
+    // padding.  Each compare is followed by its select (the fences stop the
+    // scheduler from hoisting all 64 compares, whose lane masks would then
+    // spill); this runs on the last tile only.
+    const int lim = skv - t * kBlockN - 16 * hh;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kv0 + 32 * kb + 16 * hh + r >= skv) sacc[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (32 * kb + r >= lim) sacc[kb][r] = -INFINITY;
+      }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // Weights E4M3-packed, with the tile's sum.  The tile's 32 weights per lane
   // are summed on their own before joining the running sum (see attn_fwd).
@@ -236,7 +263,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
     const float neg_m = -m_run;
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 16; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 0], cs, neg_m));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 1], cs, neg_m));
@@ -253,7 +280,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   auto exps_pow = [&]() __attribute__((always_inline)) -> float {
     float lt0 = 0.0f, lt1 = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int w = 0; w < 16; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
       const float p0 = __builtin_amdgcn_exp2f(sacc[kb][r + 0]);
       const float p1 = __builtin_amdgcn_exp2f(sacc[kb][r + 1]);
@@ -286,13 +313,17 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       slow = __any(!(lt <= 256.0f));
     }
     if (slow) {
-      float mx0 = sacc[0][0], mx1 = sacc[1][0];
+      float mx0 = sacc[0][0], mx1 = sacc[1][0], mx2 = sacc[2][0], mx3 = sacc[3][0];
 #pragma unroll
       for (int r = 1; r < 15; r += 2) {
         mx0 = vmax(vmax(mx0, sacc[0][r]), sacc[0][r + 1]);
         mx1 = vmax(vmax(mx1, sacc[1][r]), sacc[1][r + 1]);
+        mx2 = vmax(vmax(mx2, sacc[2][r]), sacc[2][r + 1]);
+        mx3 = vmax(vmax(mx3, sacc[3][r]), sacc[3][r + 1]);
       }
-      float mx = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+      mx0 = vmax(vmax(mx0, mx1), vmax(sacc[0][15], sacc[1][15]));
+      mx2 = vmax(vmax(mx2, mx3), vmax(sacc[2][15], sacc[3][15]));
+      float mx = vmax(mx0, mx2);
       mx = partner_max(mx) * cs;
       const float m_new = vmax(m_run, mx);
       const bool need = m_new > m_run + kRescaleThreshold;
@@ -319,43 +350,47 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
     l_run += lt;
   };
 
-  // ---- MFMA phase: PV(t) on 4 d-blocks, then QK(t+1) on 2 key blocks x 2
-  // channel steps.  Each step's A operand is two 16-byte LDS reads, issued two
-  // steps ahead; sched_barrier fences keep the order.
-  constexpr int kSteps = 8;
+  // ---- MFMA phase: PV(t) on 4 d-blocks x 2 key halves, then QK(t+1) on 2
+  // channel steps x 4 key blocks.  Each step's A operand is two 16-byte LDS
+  // reads, issued two steps ahead; sched_barrier fences keep the order.
+  constexpr int kSteps = 16;
   constexpr int kDist = 2;
   auto frag_off = [&](int i, int t) -> const uint8_t* {
-    if (i < 4)  // V^T rows 32 db + l32, keys [16 hh, +16) and [32 + 16 hh, +16)
-      return Vs + (t & 1) * kLdsV + (32 * i + l32) * kRowV + 16 * hh;
-    const int j = i - 4, kb = j >> 1, s = j & 1;
+    if (i < 8) {  // V^T rows 32 db + l32, keys 64 j + [16 hh, +16) and 64 j + [32 + 16 hh, +16)
+      const int db = i & 3, j = i >> 2;
+      return Vs + (t & 1) * kLdsV + (32 * db + l32) * kRowV + 64 * j + 16 * hh;
+    }
+    const int jj = i - 8, s = jj >> 2, kb = jj & 3;
     return Ks + ((t + 1) & 1) * kLdsK + (32 * kb + l32) * kRowK + 64 * s + 32 * hh;
   };
   auto frag_load = [&](int i, int t) -> i32x8 {
     const uint8_t* p = frag_off(i, t);
     const u32x4 lo = *(const u32x4*)p;
-    const u32x4 hi = *(const u32x4*)(p + (i < 4 ? 32 : 16));
+    const u32x4 hi = *(const u32x4*)(p + (i < 8 ? 32 : 16));
     return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto mfma_phase = [&](int t) {
     i32x8 fr[kDist];
 #pragma unroll
     for (int i = 0; i < kDist; ++i) fr[i] = frag_load(i, t);
-    const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const i32x8 cur = fr[i % kDist];
       if (i + kDist < kSteps) fr[i % kDist] = frag_load(i + kDist, t);
-      if (i < 4) {
-        oacc[i] = mfma_fp8(cur, pb, oacc[i]);
+      if (i < 8) {
+        const int db = i & 3, j = i >> 2;
+        const i32x8 pb = {(int)pk[8 * j + 0], (int)pk[8 * j + 1], (int)pk[8 * j + 2], (int)pk[8 * j + 3],
+                          (int)pk[8 * j + 4], (int)pk[8 * j + 5], (int)pk[8 * j + 6], (int)pk[8 * j + 7]};
+        oacc[db] = mfma_fp8(cur, pb, oacc[db]);
       } else {
-        const int j = i - 4, kb = j >> 1, s = j & 1;
+        const int jj = i - 8, s = jj >> 2, kb = jj & 3;
         sacc[kb] = mfma_fp8_scaled(cur, qreg[s], s == 0 ? (f32x16){} : sacc[kb], qk_sa, qk_sb);
       }
       if (i == 1) store_k(t + 2);
-      if (i == 2) store_v(t + 1);
-      if (i == 4) load_k(t + 3);
-      if (i == 5) load_v(t + 2);
+      if (i == 3) store_v(t + 1);
+      if (i == 6) load_k(t + 3);
+      if (i == 8) load_v(t + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -374,7 +409,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   load_v(1);
   {  // QK(0)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 4; ++kb) {
       sacc[kb] = (f32x16){};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
