@@ -190,3 +190,30 @@ def test_outlier_keys_empty_block_and_ring_slice():
     o4, l4 = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2])
     t.cuda.synchronize()
     assert t.equal(o4.view(t.int16), o.view(t.int16)) and t.equal(l4, lse)
+
+
+@pytest.mark.parametrize("lo,n", [(0, 127), (0, 128), (0, 129), (0, 192), (0, 193), (64, 129), (64, 200)])
+def test_key_counts_around_tile_halves_with_poisoned_padding(lo, n):
+    """Key blocks [lo, lo + n) of cast tensors whose codes past the readable
+    end are NaN: K rows past the block's last key, and V^T bytes past lo + n
+    rounded up to 64 tokens (all that the ABI asks to be readable).  Key
+    counts just under, at and over a 128-key tile and its 64-key halves; the
+    output must stay finite and within the FP8 contract."""
+    note(f"fp8 attention: key block [{lo}, {lo + n}) with NaN codes past the readable end")
+    t = torch()
+    B, S_q, H, S = 1, 100, 2, 512
+    q = synth.normal_bf16((B, S_q, H, 128), 110, 1)
+    kv = synth.normal_bf16((B, S, H, 128), 111, 1)
+    vv = synth.normal_bf16((B, S, H, 128), 112, 1)
+    q8, _, _, aq = lsd.cast_qkv_fp8(to_dev(q), to_dev(q), to_dev(q))
+    _, k8, v8, akv = lsd.cast_qkv_fp8(to_dev(kv), to_dev(kv), to_dev(vv))
+    t.cuda.synchronize()
+    hk, hv = codes(k8)[:, lo:lo + n], codes(v8)[:, lo:lo + n]
+    k8.view(t.uint8)[:, lo + n:] = 0x7F                            # E4M3 NaN
+    vt = v8.permute(0, 2, 3, 1)                                     # storage [B, H, D, S]
+    vt.view(t.uint8)[..., lo + (n + 63) // 64 * 64:] = 0x7F
+    o, lse = lsd.attn_fwd_fp8(q8, k8[:, lo:lo + n], v8[:, lo:lo + n], aq[0], akv[1], akv[2])
+    t.cuda.synchronize()
+    assert t.isfinite(o.float()).all() and t.isfinite(lse).all()
+    amax = np.stack([aq[0].cpu().numpy(), akv[1].cpu().numpy(), akv[2].cpu().numpy()])
+    check_fp8(o, lse, codes(q8), hk, hv, amax, range(H), all_rows(S_q), f"fp8 keys [{lo}, {lo + n})")
