@@ -82,7 +82,12 @@ __device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
   return (uint32_t)v;
 }
 // The same, writing over a dword whose old contents do not matter (both
-// halves are replaced), so no zero has to be moved in first.
+// halves are replaced), so no zero has to be moved in first.  The softmax
+// passes the first weight's own bits as that dword: its register is free once
+// the conversion has read it, so the conversions write in place.  (Passing the
+// previous tile's codes instead tied the new codes to their registers, and the
+// compiler then copied all 16 code registers out and back around the slow-path
+// test on every tile: 32 moves per tile, 3 % of the kernel's time.)
 __device__ inline uint32_t pack4_fp8_over(uint32_t old, float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
@@ -271,7 +276,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r + 3], cs, neg_m));
       lt0 = (w == 0) ? p0 + p2 : lt0 + (p0 + p2);  // no 0 + x: the first pair starts the sum
       lt1 = (w == 0) ? p1 + p3 : lt1 + (p1 + p3);
-      pk[w] = pack4_fp8_over(pk[w], p0, p1, p2, p3);  // the previous tile's codes are dead
+      pk[w] = pack4_fp8_over(__float_as_uint(p0), p0, p1, p2, p3);
     }
     return lt0 + lt1;
   };
@@ -288,7 +293,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       const float p3 = __builtin_amdgcn_exp2f(sacc[kb][r + 3]);
       lt0 = (w == 0) ? p0 + p2 : lt0 + (p0 + p2);
       lt1 = (w == 0) ? p1 + p3 : lt1 + (p1 + p3);
-      pk[w] = pack4_fp8_scaled(pk[w], p0, p1, p2, p3, m_pow);
+      pk[w] = pack4_fp8_scaled(__float_as_uint(p0), p0, p1, p2, p3, m_pow);
     }
     return lt0 + lt1;
   };
