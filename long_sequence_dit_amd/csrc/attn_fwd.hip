@@ -174,6 +174,40 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
     vst[par()][0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
     vst[par()][1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
   };
+  // The loop's loads (K of tile t + 4 and V of tile t + 3 in iteration t)
+  // take descriptors prepared in the softmax phase, whose wave has issue
+  // slots to spare, instead of ahead of the MFMA phase's loads; 32-bit byte
+  // counts (the host keeps sequence strides below 2^24 elements), scalar
+  // compares, and an empty asm that keeps the work there.
+  uint32_t nk_lo = 0, nk_hi = 0, nk_n = 0, nv_lo = 0, nv_hi = 0, nv_n = 0;
+  auto tile_bytes32 = [&](int t, int ss) -> uint32_t {
+    const int rows = skv - t * kBlockN;
+    return rows >= kBlockN ? (uint32_t)((kBlockN - 1) * ss * 2 + 2 * D)
+                           : (rows > 0 ? (uint32_t)((rows - 1) * ss * 2 + 2 * D) : 0u);
+  };
+  auto prep_loads = [&](int t) {
+    const uint64_t kp = (uint64_t)(uintptr_t)(kbase + (int64_t)(t + 4) * kBlockN * a.k_ss);
+    const uint64_t vp = (uint64_t)(uintptr_t)(vbase + (int64_t)(t + 3) * kBlockN * a.v_ss);
+    nk_lo = __builtin_amdgcn_readfirstlane((uint32_t)kp);
+    nk_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kp >> 32));
+    nk_n = __builtin_amdgcn_readfirstlane(tile_bytes32(t + 4, (int)a.k_ss));
+    nv_lo = __builtin_amdgcn_readfirstlane((uint32_t)vp);
+    nv_hi = __builtin_amdgcn_readfirstlane((uint32_t)(vp >> 32));
+    nv_n = __builtin_amdgcn_readfirstlane(tile_bytes32(t + 3, (int)a.v_ss));
+    asm volatile("" : "+s"(nk_lo), "+s"(nk_hi), "+s"(nk_n), "+s"(nv_lo), "+s"(nv_hi), "+s"(nv_n));
+  };
+  auto load_k_pre = [&](auto par) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(((uint64_t)nk_hi << 32) | nk_lo), (short)0, (int)nk_n, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < C::kLoadsPerThread; ++u) kst[par()][u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_off[u], 0, 0);
+  };
+  auto load_v_pre = [&](auto par) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(((uint64_t)nv_hi << 32) | nv_lo), (short)0, (int)nv_n, 0x00020000);
+    vst[par()][0] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off0, 0, 0);
+    vst[par()][1] = __builtin_amdgcn_raw_buffer_load_b128(r, v_off1, 0, 0);
+  };
   auto store_k = [&](int t, auto par) {
 #pragma unroll
     for (int u = 0; u < C::kLoadsPerThread; ++u)
@@ -326,8 +360,8 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
       // ahead of their stores
       if (i == 2) store_k(t + 2, P{});
       if (i == 3) store_v(t + 1, Q{});
-      if (i == 6) load_k(t + 4, P{});
-      if (i == 8) load_v(t + 3, Q{});
+      if (i == 6) load_k_pre(P{});
+      if (i == 8) load_v_pre(Q{});
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -373,6 +407,7 @@ attn_fwd_kernel(const AttnArgs a, int n_qtiles) {
   auto iteration = [&](int t, auto par) {
     if ((t + 1) * kBlockN > skv) mask_tail(t);
     softmax();
+    prep_loads(t);
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
     mfma_phase(t, par);

@@ -248,8 +248,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   };
   auto dma_k_next = [&](auto off_c) {
     constexpr int kOff = decltype(off_c)::value;
-    const int rows = k_rows_next;
-    rk[2] = rows >= kBlockN ? k_full : (rows > 0 ? (uint32_t)((rows - 1) * (int)a.k_ss * 2 + 2 * D) : 0u);
+    // (rk[2], the tile's byte range, was set in the softmax phase)
     // (a second slot's K rows lie 8 or more token strides in: offset >= 2048)
     if constexpr (C::kDma > 1) dma16_asm_pair<kOff>(rk, wbase, k_voff[0], k_voff[1] - 1024u);
     else dma16_asm<kOff>(rk, wbase, k_voff[0]);
@@ -259,6 +258,17 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
   const uint64_t v_first = (uint64_t)(uintptr_t)(vbase + (kStages - 1) * kBlockN);  // V_{t+3} in iteration t
   u32x4s rv = {(uint32_t)v_first, (uint32_t)(v_first >> 32) & 0xffffu, (uint32_t)vt_range, 0x00020000u};
   int v_key_next = (kStages - 1) * kBlockN;
+  int v_full = 0;
+  // Scalar bookkeeping of the next loads, done in the softmax phase (whose
+  // wave has issue slots to spare) rather than ahead of the first MFMA of the
+  // MFMA phase; the empty asm keeps it there.
+  auto prep_next = [&]() {
+    const int rows = k_rows_next;
+    rk[2] = __builtin_amdgcn_readfirstlane(
+        rows >= kBlockN ? k_full : (rows > 0 ? (uint32_t)((rows - 1) * (int)a.k_ss * 2 + 2 * D) : 0u));
+    v_full = __builtin_amdgcn_readfirstlane((v_key_next + kBlockN <= skv) ? 1 : 0);
+    asm volatile("" : "+s"(rk[2]), "+s"(v_full));
+  };
   auto dma_v_next = [&](auto off_c) {
     constexpr int kOff = decltype(off_c)::value;
     auto issue = [&](uint32_t o0, uint32_t o1) {
@@ -274,7 +284,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
         dma16_asm<kOff>(rv, wbase, o0);
       }
     };
-    if (v_key_next + kBlockN <= skv) {  // uniform: every chunk of the tile is valid
+    if (v_full) {  // uniform: every chunk of the tile is valid (set in the softmax phase)
       issue(v_voff[0], C::kDma > 1 ? v_voff[C::kDma - 1] : 0u);
     } else {
       auto voff = [&](int u) { return (v_key_next + v_key[u] + 8 <= skv) ? v_voff[u] : 0x7ffffff0u; };
@@ -504,6 +514,7 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
       }
     }
     softmax();
+    prep_next();
     prefetch(st);  // stage t was published before SM(t) began
     // No LDS wait before this barrier: the wave has written no LDS in SM(t),
     // and its prefetch reads of stage t need not land before the other group
