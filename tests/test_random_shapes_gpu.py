@@ -83,3 +83,29 @@ def test_random_case(i, B, S_q, S_kv, H, D, tok, lens, scale):
             lsd.attn_fwd_accumulate(q, kb, vb, oa, la, o=o2, scale=sc)
         t.cuda.synchronize()
         assert_attention_close(to_f64(o2), O, la.cpu().numpy(), L, f"case {i}, two Ring steps")
+
+
+# A second sweep whose token-contiguous V pitches straddle 64 keys: the kernel
+# pairs a thread's two V^T loads per tile only when the pitch is at least 64,
+# so both variants run, with padding up to 120 keys past the rounded length.
+PITCH_CASES = [(c, int(e)) for c, e in
+               zip(_cases(40, 77731), np.random.default_rng(77732).choice([0, 8, 56, 64, 120], 40))]
+
+
+@pytest.mark.parametrize("case,extra", PITCH_CASES)
+def test_random_case_pitches(case, extra):
+    i, B, S_q, S_kv, H, D, _, lens, scale = case
+    note(f"pitch case {i}: B={B} S_q={S_q} S_kv={S_kv} H={H} D={D} extra={extra} lens={lens} scale={scale}")
+    t = torch()
+    seed = 8000 + 10 * i
+    qh = synth.normal_bf16((B, S_q, H, D), seed, 1)
+    kh = synth.normal_bf16((B, S_kv, H, D), seed + 1, 1)
+    vh = synth.normal_bf16((B, S_kv, H, D), seed + 2, 1)
+    q, k = to_dev(qh), to_dev(kh)
+    v = _token_major(to_dev(vh), extra)
+    lsd_lens = t.tensor(lens, dtype=t.int32, device="cuda") if lens is not None else None
+    sc = None if scale == 0.0 else scale
+    o, lse = lsd.attn_fwd(q, k, v, scale=sc, kv_lens=lsd_lens)
+    t.cuda.synchronize()
+    O, L = ref.attention(qh, kh, vh, scale=sc, kv_lens=lens)
+    assert_attention_close(to_f64(o), O, lse.cpu().numpy(), L, f"pitch case {i}")
