@@ -17,7 +17,12 @@
 // take n * heads * 2 floats of LDS, sized at launch: a fixed 64 KB allowed
 // only two workgroups per CU and ran 40 % slower.  Workgroups of 512 threads:
 // at n = 3 (the Ring share) 0.181 ms against 0.193 ms with 256 threads, at
-// n = 2 (LTX-2 scale) 0.108 against 0.111 ms.
+// n = 2 (LTX-2 scale) 0.108 against 0.111 ms.  For n = 2 to 4 the partial
+// count is a template constant and each thread issues its vector's n loads
+// before any arithmetic (with a run-time count the compiler issued one load
+// at a time and waited for it): 0.181 -> 0.174 ms at n = 3 (72 -> 75 % of
+// HBM), 0.108 -> 0.103 ms at n = 2 (71 -> 74 %), bit-identical.  Two vectors
+// per thread per pass were slower at n = 2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +50,9 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 // streams the token rows: for contiguous (B, S, H, D) partials a token's heads
 // are adjacent, so the workgroup reads and writes kTok * hg * D * 2 contiguous
 // bytes per partial, not scattered 256-byte rows.
+// kN: the partial count when it is a compile-time constant (2 to 4), else 0
+// (then the partials are read in a run-time loop).
+template <int kN>
 __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a, int n_stiles, int hg, int n_hgroups) {
   extern __shared__ float w_s[];  // [n][hg][kTok], sized at launch
 
@@ -86,25 +94,48 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a,
   const int vpr = a.D >> 3;          // 16-byte vectors per head row
   const int vpt = nh * vpr;          // per token
   const int ns = min(kTok, a.S - s0);
-  for (int q = tid; q < ns * vpt; q += kThreads) {
+  auto addr_in = [&](int i, int q) -> const u32x4* {
     const int sl = q / vpt, r = q % vpt;
     const int hl = r / vpr, c = r % vpr;
-    const int s = s0 + sl, h = h0 + hl;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < a.n; ++i) {
-      const float w = w_s[(i * hg + hl) * kTok + sl];
-      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.o_in[i] + (int64_t)b * a.in_sb[i] +
-                                                                 (int64_t)s * a.in_ss[i] + (int64_t)h * a.in_sh[i] + 8 * c));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += w * __uint_as_float(v[e] << 16);
-        acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xffff0000u);
-      }
-    }
+    return (const u32x4*)(a.o_in[i] + (int64_t)b * a.in_sb[i] + (int64_t)(s0 + sl) * a.in_ss[i] +
+                          (int64_t)(h0 + hl) * a.in_sh[i] + 8 * c);
+  };
+  auto store = [&](int q, const float* acc) {
+    const int sl = q / vpt, r = q % vpt;
+    const int hl = r / vpr, c = r % vpr;
     const u32x4 out = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
                        pack_bf16(acc[6], acc[7])};
-    __builtin_nontemporal_store(out, (u32x4*)(a.o_out + (int64_t)b * a.out_sb + (int64_t)s * a.out_ss +
-                                              (int64_t)h * a.out_sh + 8 * c));
+    __builtin_nontemporal_store(out, (u32x4*)(a.o_out + (int64_t)b * a.out_sb + (int64_t)(s0 + sl) * a.out_ss +
+                                              (int64_t)(h0 + hl) * a.out_sh + 8 * c));
+  };
+  auto weight = [&](int i, int q) {
+    const int sl = q / vpt, hl = (q % vpt) / vpr;
+    return w_s[(i * hg + hl) * kTok + sl];
+  };
+  auto accumulate = [&](float* acc, float w, const u32x4& v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * __uint_as_float(v[e] << 16);
+      acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xffff0000u);
+    }
+  };
+  const int nq = ns * vpt;
+  if constexpr (kN > 0) {
+    for (int q = tid; q < nq; q += kThreads) {
+      u32x4 v[kN];
+#pragma unroll
+      for (int i = 0; i < kN; ++i) v[i] = __builtin_nontemporal_load(addr_in(i, q));
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kN; ++i) accumulate(acc, weight(i, q), v[i]);
+      store(q, acc);
+    }
+  } else {
+    for (int q = tid; q < nq; q += kThreads) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < a.n; ++i) accumulate(acc, weight(i, q), __builtin_nontemporal_load(addr_in(i, q)));
+      store(q, acc);
+    }
   }
 }
 
@@ -118,8 +149,19 @@ hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)n_stiles * n_hgroups * a.B;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)a.n * hg * kTok * sizeof(float);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg,
-                     n_hgroups);
+  switch (a.n) {
+    case 2:
+      hipLaunchKernelGGL(attn_merge_kernel<2>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg, n_hgroups);
+      break;
+    case 3:
+      hipLaunchKernelGGL(attn_merge_kernel<3>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg, n_hgroups);
+      break;
+    case 4:
+      hipLaunchKernelGGL(attn_merge_kernel<4>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg, n_hgroups);
+      break;
+    default:
+      hipLaunchKernelGGL(attn_merge_kernel<0>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, a, n_stiles, hg, n_hgroups);
+  }
   return hipGetLastError();
 }
 
