@@ -243,6 +243,10 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
   float m_run = -INFINITY;  // an integer on the power-of-two path once set
   float m_pow = 0.0f, m_inv = 0.0f, m_lim = 0.0f;  // 2^m, 2^-m, 2^(m+8) for the power-of-two path
+  // wave-uniform: the power-of-two path applies (every lane's |m| <= 100);
+  // m only changes in the slow path, which updates this (false until the
+  // first tile has set m)
+  bool fast_ok = false;
   float l_run = 0.0f;
   f32x16 sacc[4];
   uint32_t pk[16] = {};  // this tile's weights as E4M3, in PV operand order (two 64-key halves)
@@ -309,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
     // power-of-two path with |m| <= 100 (wave-uniform): exp2(s) cannot
     // overflow while weights stay <= 2^8 relative to m, nor underflow for
     // the row's larger weights
-    if (pow2 && __all(m_run >= -100.0f && m_run <= 100.0f)) {
+    if (fast_ok) {
       lt = exps_pow();
       slow = __any(!(lt <= m_lim));
       lt *= m_inv;
@@ -349,6 +353,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
           m_inv = ldexpf(1.0f, -mi);
           m_lim = ldexpf(1.0f, mi + 8);
         }
+        fast_ok = pow2 && __all(m_run >= -100.0f && m_run <= 100.0f);
       }
       lt = exps();
     }
