@@ -33,8 +33,10 @@
 //   max is taken only when its weights against the current reference could
 //   exceed 2^8, so most tiles skip it.
 // * The MFMA phase issues the next tiles' direct loads from inline assembly
-//   with every operand already scalar (M0 set by one scalar add), because each
-//   non-MFMA instruction in that phase delays the MFMA stream.
+//   with every operand already scalar (one M0 write per pair of loads, their
+//   byte ranges and validity worked out in the softmax phase), because each
+//   non-MFMA instruction in that phase delays the MFMA stream; the two
+//   phases now take about equally long.
 // * blockIdx is remapped so that consecutive query tiles of one (b, h) land on
 //   the same XCD and share its L2 while streaming the same K/V.
 #include <hip/hip_runtime.h>
