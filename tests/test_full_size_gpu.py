@@ -243,3 +243,25 @@ def test_cosmos_ulysses_step_as_benchmarked():
     t.cuda.synchronize()
     host = [to_bits(x) for x in [o] + others]
     assert np.array_equal(to_bits(shard), ref.relayout_head_to_seq(host, P, 0)), "inverse relayout shard 0"
+
+
+def test_cosmos_scale_fp8_with_outlier_keys():
+    """The largest configuration on the FP8 path: the Cosmos3-Super share
+    (150,000 tokens, 16 heads) whose 1 % outlier keys (x4) set K's per-head
+    scale, so every other key is quantised four times more coarsely; codes
+    and amax bit-exact against the oracle's cast, attention within the FP8
+    contract on the sampled rows of every head."""
+    note("full Cosmos3-Super share on the FP8 path: cast + FP8 attention, B=1 S=150000 H=16, 1% keys x4")
+    from test_fp8_gpu import check_fp8, codes
+    from oracle import fp8 as ofp8
+    t = torch()
+    q, k, v, _ = synth.cosmos_qkv()
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(to_dev(q), to_dev(k), to_dev(v))
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2])
+    t.cuda.synchronize()
+    eq8, ek8, ev8, eamax = ofp8.cast_qkv(q, k, v)
+    hq, hk, hv = codes(q8), codes(k8), codes(v8)
+    assert np.array_equal(amax.cpu().numpy(), eamax) and np.array_equal(hq, eq8)
+    assert np.array_equal(hk, ek8) and np.array_equal(hv, ev8)
+    del q8, k8, v8
+    check_fp8(o, lse, hq, hk, hv, eamax, range(16), lambda b, h: sample_rows(150_000, 400 + h), "Cosmos fp8")
