@@ -322,13 +322,19 @@ attn_fwd_vt_kernel(const AttnArgs a, int n_qtiles) {
 
   // ---- VALU phase SM(t): mask, row max, lazy rescale, exp
   auto mask_tail = [&](int t) {
-    const int kv0 = t * kBlockN;
+    // Register r of key block kb holds key t kBlockN + 32 kb + 16 (r / 8) +
+    // 8 hh + r % 8; it is padding from lim on.  Each select is pinned where
+    // it stands (empty asm): left to the compiler, the compares all came
+    // first and their lane masks spilled.
+    const int lim = skv - t * kBlockN - 8 * hh;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = kv0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-        if (j >= skv) sacc[kb][r] = -INFINITY;
+        float x = sacc[kb][r];
+        if (32 * kb + 16 * (r >> 3) + (r & 7) >= lim) x = -INFINITY;
+        asm volatile("" : "+v"(x));
+        sacc[kb][r] = x;
       }
   };
   // P = exp2(S c - m) rounded to bf16, with m the current reference max.  The
