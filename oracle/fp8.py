@@ -24,6 +24,13 @@ Readings where the pages are silent (also in the design notes):
   then apply that factor exactly on the matrix cores.
 * FP8 attention computes the attention of the dequantised inputs: its
   definition is ``attention`` applied to them.
+* Key-length mask (the bf16 path's key-only padding mask, carried over):
+  with ``kv_lens``, batch entry b has kv_lens[b] valid keys (clamped to
+  [0, S]).  K's and V's amax are taken over the valid tokens only, V's codes
+  of the padding tokens are zero, and K's codes of the padding tokens are
+  outside the contract (the library leaves them unwritten; the attention
+  never reads them).  Q is unaffected: every query row attends to the valid
+  keys of its batch entry.
 """
 
 from __future__ import annotations
@@ -79,6 +86,25 @@ def head_amax(x) -> np.ndarray:
     return v.max(axis=(1, 3)) if v.shape[1] > 0 else np.zeros((v.shape[0], v.shape[2]))
 
 
+def valid_lengths(kv_lens, B: int, S: int) -> np.ndarray:
+    """kv_lens clamped to [0, S] per batch entry (all S without a mask)."""
+    if kv_lens is None:
+        return np.full(B, S, dtype=np.int64)
+    return np.clip(np.asarray(kv_lens, dtype=np.int64).reshape(B), 0, S)
+
+
+def head_amax_valid(x, lens) -> np.ndarray:
+    """``head_amax`` over the first lens[b] tokens of each batch entry b
+    (zero where there are none): [B, H]."""
+    x = np.asarray(x)
+    out = np.zeros((x.shape[0], x.shape[2]))
+    for b in range(x.shape[0]):
+        n = int(lens[b])
+        if n > 0:
+            out[b] = head_amax(x[b:b + 1, :n])[0]
+    return out
+
+
 # log2(e) / sqrt(128) in float32: the default logit factor of the attention
 # (the softmax scale 1 / sqrt(D) for D = 128, times log2 e, rounded to float32)
 SCALE_LOG2_D128 = np.float32(float(np.float32(1.0 / np.sqrt(128.0))) * 1.4426950408889634074)
@@ -117,12 +143,24 @@ def quantize(x, amax: np.ndarray) -> np.ndarray:
     return e4m3_encode(prod)
 
 
-def cast_qkv(q, k, v):
+def cast_qkv(q, k, v, kv_lens=None):
     """The single FP8 cast pass over Q, K, V: codes for each tensor and the
-    amax array [3, B, H] (q's entry the scale amax of ``q_scale_amax``, k, v)."""
-    amax = np.stack([head_amax(q), head_amax(k), head_amax(v)]).astype(np.float32)
+    amax array [3, B, H] (q's entry the scale amax of ``q_scale_amax``, k, v).
+    With ``kv_lens`` (the key-length mask): K's and V's amax over the valid
+    tokens, V's codes of the padding tokens zero; K's codes of the padding
+    tokens are returned as computed but are outside the contract."""
+    if kv_lens is None:
+        amax = np.stack([head_amax(q), head_amax(k), head_amax(v)]).astype(np.float32)
+    else:
+        lens = valid_lengths(kv_lens, np.asarray(k).shape[0], np.asarray(k).shape[1])
+        amax = np.stack([head_amax(q), head_amax_valid(k, lens), head_amax_valid(v, lens)]).astype(np.float32)
     amax[0] = q_scale_amax(amax[0], amax[1])
-    return quantize(q, amax[0]), quantize(k, amax[1]), quantize(v, amax[2]), amax
+    with np.errstate(invalid="ignore"):
+        q8, k8, v8 = quantize(q, amax[0]), quantize(k, amax[1]), quantize(v, amax[2])
+    if kv_lens is not None:
+        for b in range(v8.shape[0]):
+            v8[b, lens[b]:] = 0
+    return q8, k8, v8, amax
 
 
 def dequantize(codes, amax) -> np.ndarray:
@@ -131,19 +169,23 @@ def dequantize(codes, amax) -> np.ndarray:
     return e4m3_decode(codes) * s.astype(np.float64)[:, None, :, None]
 
 
-def attention_fp8(q8, k8, v8, q_amax, k_amax, v_amax, scale=None):
+def attention_fp8(q8, k8, v8, q_amax, k_amax, v_amax, scale=None, kv_lens=None):
     """Attention over the dequantised FP8 inputs (codes [B, S, H, D] and
-    per-(batch, head) amax): (O, LSE) float64."""
-    return ref.attention(dequantize(q8, q_amax), dequantize(k8, k_amax), dequantize(v8, v_amax), scale)
+    per-(batch, head) amax): (O, LSE) float64; ``kv_lens`` is the key-length
+    mask of ``ref.attention``."""
+    return ref.attention(dequantize(q8, q_amax), dequantize(k8, k_amax), dequantize(v8, v_amax), scale,
+                         kv_lens=kv_lens)
 
 
-def attention_fp8_rows(q8, k8, v8, q_amax, k_amax, v_amax, b: int, h: int, rows, scale=None):
-    """``attention_fp8`` for selected query rows of one (batch, head)."""
+def attention_fp8_rows(q8, k8, v8, q_amax, k_amax, v_amax, b: int, h: int, rows, scale=None, kv_len=None):
+    """``attention_fp8`` for selected query rows of one (batch, head), over
+    the first ``kv_len`` keys (all of them by default)."""
     sq = np.float32(np.float32(q_amax[b, h]) / np.float32(E4M3_MAX))
     sk = np.float32(np.float32(k_amax[b, h]) / np.float32(E4M3_MAX))
     sv = np.float32(np.float32(v_amax[b, h]) / np.float32(E4M3_MAX))
     rows = np.asarray(list(rows), dtype=np.int64)
     qh = e4m3_decode(q8[b, rows, h, :]) * float(sq)
-    kh = e4m3_decode(k8[b, :, h, :]) * float(sk)
-    vh = e4m3_decode(v8[b, :, h, :]) * float(sv)
+    n = k8.shape[1] if kv_len is None else int(np.clip(kv_len, 0, k8.shape[1]))
+    kh = e4m3_decode(k8[b, :n, h, :]) * float(sk)
+    vh = e4m3_decode(v8[b, :n, h, :]) * float(sv)
     return ref._attend_block(qh, kh, vh, ref._default_scale(q8.shape[3], scale))

@@ -600,5 +600,56 @@ def pin_fp8_attention():
     assert np.allclose(o_r, O[0, rows, 1], rtol=0, atol=1e-12) and np.allclose(l_r, L[0, 1, rows], rtol=0, atol=1e-12)
 
 
-FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_q_scale, pin_fp8_attention]
+def pin_fp8_key_lengths():
+    """The key-length mask on the FP8 path reduces to the unmasked cast and
+    attention of the valid keys alone: per batch entry, the masked cast's
+    amax and its Q, K and V codes of valid tokens equal the unmasked cast of
+    Q with K and V cut to their first kv_lens[b] tokens; V's padding codes
+    are zero; an entry without keys has K and V amax 0 (Q keeps its amax);
+    NaN in the padding changes nothing; lengths are clamped to [0, S]; with
+    every length S the masked cast is the unmasked one; the masked attention
+    equals attention over the cut keys."""
+    from oracle import fp8
+    B, S, H, D = 4, 70, 2, 64
+    q = _rand((B, S, H, D), 61)
+    k = _rand((B, S, H, D), 62).copy()
+    v = _rand((B, S, H, D), 63).copy()
+    lens = [70, 33, 0, 1]
+    nan_bits = np.uint16(0x7FC1)
+    for b, n in enumerate(lens):
+        k[b, n:] = nan_bits
+        v[b, n:] = nan_bits
+    q8, k8, v8, amax = fp8.cast_qkv(q, k, v, kv_lens=lens)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(amax[1:, b] == 0) and np.all(v8[b] == 0)
+            assert np.array_equal(amax[0, b], fp8.head_amax(q[b:b + 1])[0].astype(np.float32))
+            continue
+        tq, tk, tv, ta = fp8.cast_qkv(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n])
+        assert np.array_equal(amax[:, b], ta[:, 0])
+        assert np.array_equal(q8[b], tq[0]) and np.array_equal(k8[b, :n], tk[0]) and np.array_equal(v8[b, :n], tv[0])
+        assert np.all(v8[b, n:] == 0)
+    # clamping, and the mask at full length
+    _, _, _, a_clamp = fp8.cast_qkv(q, k, v, kv_lens=[100, 33, -5, 1])
+    assert np.array_equal(a_clamp, amax)
+    kk, vv = _rand((B, S, H, D), 62), _rand((B, S, H, D), 63)
+    full = fp8.cast_qkv(q, kk, vv, kv_lens=[S] * B)
+    ref_full = fp8.cast_qkv(q, kk, vv)
+    assert all(np.array_equal(x, y) for x, y in zip(full, ref_full))
+    # attention over the valid keys (entries with keys)
+    O, L = fp8.attention_fp8(q8, k8, v8, amax[0], amax[1], amax[2], kv_lens=lens)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(O[b] == 0) and np.all(np.isneginf(L[b]))
+            continue
+        Ob, Lb = fp8.attention_fp8(q8[b:b + 1], k8[b:b + 1, :n], v8[b:b + 1, :n], amax[0, b:b + 1], amax[1, b:b + 1],
+                                   amax[2, b:b + 1])
+        assert np.array_equal(O[b], Ob[0]) and np.array_equal(L[b], Lb[0])
+        o_r, l_r = fp8.attention_fp8_rows(q8, k8, v8, amax[0], amax[1], amax[2], b, 1, [0, 69], kv_len=n)
+        assert np.allclose(o_r, O[b, [0, 69], 1], rtol=0, atol=1e-12) and np.allclose(l_r, L[b, 1, [0, 69]], rtol=0,
+                                                                                       atol=1e-12)
+
+
+FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_q_scale, pin_fp8_attention,
+            pin_fp8_key_lengths]
 ALL_PINS = ALL_PINS + FP8_PINS

@@ -310,7 +310,19 @@ def _qscale_power_too_high(amax_q, amax_k):
     return np.where(np.asarray(amax_q) > 0, r * np.float32(2.0), r).astype(np.float32)
 
 
-FP8_MUTANTS = [("e4m3_encode", _encode_ties_away), ("e4m3_encode", _encode_truncate),
+_orig_amax_valid = _fp8.head_amax_valid
+
+
+def _amax_valid_ignores_lengths(x, lens):
+    return _orig_head_amax(x)
+
+
+def _amax_valid_one_short(x, lens):
+    return _orig_amax_valid(x, np.maximum(np.asarray(lens) - 1, 0))
+
+
+FP8_MUTANTS = [("head_amax_valid", _amax_valid_ignores_lengths), ("head_amax_valid", _amax_valid_one_short),
+               ("e4m3_encode", _encode_ties_away), ("e4m3_encode", _encode_truncate),
                ("e4m3_decode", _decode_fnuz_bias), ("head_amax", _amax_per_tensor),
                ("dequantize", _dequant_no_scale), ("q_scale_amax", _qscale_identity),
                ("q_scale_amax", _qscale_no_log2e), ("q_scale_amax", _qscale_uses_q),
