@@ -12,6 +12,8 @@
  *   lsd_attn_merge            exact log-sum-exp merge of partial (O, LSE)
  *   lsd_cast_qkv_fp8          one FP8 cast of Q, K, V (per-head scales)
  *   lsd_attn_fwd_fp8          attention on the FP8 inputs
+ *   lsd_cast_qkv_fp8_masked   the cast with a per-batch key count
+ *   lsd_attn_fwd_fp8_masked   FP8 attention with a per-batch key count
  *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
  *                             after attention)
  *
@@ -53,8 +55,10 @@ extern "C" {
 #endif
 
 /* 2: lsd_cast_qkv_fp8 stores Q's scale amax (a power-of-two logit factor)
- *    in place of Q's plain amax; signatures unchanged from 1. */
-#define LSD_ABI_VERSION 2
+ *    in place of Q's plain amax; signatures unchanged from 1.
+ * 3: adds lsd_cast_qkv_fp8_masked and lsd_attn_fwd_fp8_masked (the key-length
+ *    mask on the FP8 path); earlier entry points unchanged. */
+#define LSD_ABI_VERSION 3
 
 typedef enum lsd_status {
   LSD_OK = 0,
@@ -259,6 +263,38 @@ lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* a
 lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
                             const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
                             float softmax_scale, void* stream);
+
+/*
+ * The FP8 cast and FP8 attention with the key-only padding mask of
+ * lsd_attn_fwd_masked (defined by "How 8 GPUs split tokens: what LTX-2's
+ * sequence-parallel all2all moves", "Data flow": padding keys get zero
+ * weight, every query row sees all valid keys of its batch entry), combined
+ * with the single FP8 cast of "Scaling Video Generation Across NVL72 rack
+ * with TensorRT-LLM", "Ulysses Parallelism > Fused vs. unfused QKV
+ * all-to-all"; the per-head scales then come from the valid tokens alone.
+ *
+ *   kv_lens  int32 device array of B entries, 4-byte aligned, not NULL;
+ *            batch entry b has kv_lens[b] valid keys (clamped to [0, S]);
+ *            it may not overlap any output
+ *
+ * lsd_cast_qkv_fp8_masked: as lsd_cast_qkv_fp8, except that K's and V's amax
+ * are taken over the valid tokens only (0 for an entry without keys, which
+ * also leaves Q's amax unadjusted), V's codes of the tokens from kv_lens[b]
+ * to the padded row end are zero, and K's codes of the tokens from
+ * kv_lens[b] on are not written.  Padding may hold any bits (NaN included).
+ *
+ * lsd_attn_fwd_fp8_masked: as lsd_attn_fwd_fp8 over the first kv_lens[b] keys
+ * of batch entry b; K rows past them are not read, V rows are read up to
+ * kv_lens[b] rounded up to 64 tokens and must hold finite codes there (the
+ * masked cast writes zeros).  An entry with kv_lens[b] == 0 gives O = 0 and
+ * LSE = -inf.
+ */
+lsd_status lsd_cast_qkv_fp8_masked(const lsd_view4* src, const lsd_view4* dst, float* amax, const int32_t* kv_lens,
+                                   void* stream);
+lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
+                                   const float* q_amax, const float* k_amax, const float* v_amax,
+                                   const int32_t* kv_lens, const lsd_view4* o, float* lse, float softmax_scale,
+                                   void* stream);
 
 /*
  * Ulysses sequence-major -> head-major relayout for one destination rank.

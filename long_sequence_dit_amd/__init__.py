@@ -64,6 +64,12 @@ def lib():
         L.lsd_attn_fwd_fp8.restype = ctypes.c_int
         L.lsd_attn_fwd_fp8.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, P(View4), ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+        L.lsd_cast_qkv_fp8_masked.restype = ctypes.c_int
+        L.lsd_cast_qkv_fp8_masked.argtypes = [P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.lsd_attn_fwd_fp8_masked.restype = ctypes.c_int
+        L.lsd_attn_fwd_fp8_masked.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, P(View4), ctypes.c_void_p,
+                                              ctypes.c_float, ctypes.c_void_p]
         L.lsd_relayout_head_to_seq.restype = ctypes.c_int
         L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
@@ -253,27 +259,36 @@ def fp8_buffers(B, S, H, D=128, device="cuda"):
     return q8, k8, v8, amax
 
 
-def cast_qkv_fp8(q, k, v, out=None):
+def cast_qkv_fp8(q, k, v, out=None, kv_lens=None):
     """One FP8 (E4M3) cast of Q, K, V (bf16 (B, S, H, D) views) with one scale
     per (tensor, batch, head).  Returns (q8, k8, v8, amax): v8 is a (B, S, H, D)
     view of V stored transposed; amax[t] is tensor t's per-(b, h) scale amax
     (K, V: max |x|; Q: the power-of-two-adjusted value in [amax_q, 2 amax_q)
-    described in include/lsd.h)."""
+    described in include/lsd.h).  ``kv_lens`` (int32 [B] on the GPU) is the
+    key-length mask: K and V scales from the first kv_lens[b] tokens, V codes
+    of the rest zero, K codes of the rest not written."""
     B, S, H, D = q.shape
     if out is None:
         out = fp8_buffers(B, S, H, D, q.device)
     q8, k8, v8, amax = out
     sv = (View4 * 3)(_view(q, "q"), _view(k, "k"), _view(v, "v"))
     dv = (View4 * 3)(_view8(q8, "q8"), _view8(k8, "k8"), _view8(v8, "v8"))
-    st = lib().lsd_cast_qkv_fp8(sv, dv, _f32_ptr(amax, "amax", (3, B, H)), _stream(q))
-    _check(st, "lsd_cast_qkv_fp8")
+    ap = _f32_ptr(amax, "amax", (3, B, H))
+    if kv_lens is None:
+        st = lib().lsd_cast_qkv_fp8(sv, dv, ap, _stream(q))
+        _check(st, "lsd_cast_qkv_fp8")
+    else:
+        st = lib().lsd_cast_qkv_fp8_masked(sv, dv, ap, _lens_ptr(kv_lens, B), _stream(q))
+        _check(st, "lsd_cast_qkv_fp8_masked")
     return q8, k8, v8, amax
 
 
 def attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o=None, lse=None, scale: Optional[float] = None,
-                 return_lse: bool = True):
+                 return_lse: bool = True, kv_lens=None):
     """Attention over FP8 inputs (as ``cast_qkv_fp8`` produces them): the
-    attention of the dequantised values, O in bf16 and the LSE."""
+    attention of the dequantised values, O in bf16 and the LSE.  ``kv_lens``
+    (int32 [B] on the GPU): batch entry b attends only its first kv_lens[b]
+    keys."""
     torch = _torch()
     B, S_q, H, D = q8.shape
     if o is None:
@@ -283,9 +298,15 @@ def attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o=None, lse=None, scale: Op
     qv, kv, vv, ov = _view8(q8, "q8"), _view8(k8, "k8"), _view8(v8, "v8"), _view(o, "o")
     pq, pk, pv = (_f32_ptr(x, n, (B, H)) for x, n in ((q_amax, "q_amax"), (k_amax, "k_amax"), (v_amax, "v_amax")))
     lp = _f32_ptr(lse, "lse", (B, H, S_q)) if lse is not None else None
-    st = lib().lsd_attn_fwd_fp8(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pq, pk, pv, ctypes.byref(ov),
-                                lp, ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q8))
-    _check(st, "lsd_attn_fwd_fp8")
+    sc = ctypes.c_float(0.0 if scale is None else float(scale))
+    if kv_lens is None:
+        st = lib().lsd_attn_fwd_fp8(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pq, pk, pv,
+                                    ctypes.byref(ov), lp, sc, _stream(q8))
+        _check(st, "lsd_attn_fwd_fp8")
+    else:
+        st = lib().lsd_attn_fwd_fp8_masked(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pq, pk, pv,
+                                           _lens_ptr(kv_lens, B), ctypes.byref(ov), lp, sc, _stream(q8))
+        _check(st, "lsd_attn_fwd_fp8_masked")
     return (o, lse) if lse is not None else o
 
 

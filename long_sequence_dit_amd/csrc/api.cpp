@@ -247,7 +247,8 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), acc ? "attn_fwd_accumulate" : "attn_fwd");
 }
 
-lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream) {
+lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, const int32_t* kv_lens,
+                        void* stream) {
   if (src == nullptr || dst == nullptr) return fail(LSD_EINVAL, "null src or dst array");
   lsd_status s;
   static const char* sn[3] = {"src[0] (q)", "src[1] (k)", "src[2] (v)"};
@@ -267,18 +268,21 @@ lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax,
                 (long long)dst[2].stride[3], (long long)S);
   if (amax == nullptr) return fail(LSD_EINVAL, "null amax");
   if ((uintptr_t)amax % 4 != 0) return fail(LSD_EINVAL, "amax not 4-byte aligned");
+  if (kv_lens != nullptr && (uintptr_t)kv_lens % 4 != 0) return fail(LSD_EINVAL, "kv_lens not 4-byte aligned");
   if (B * H == 0) return ok();
-  Span ins[3], outs[4];
+  Span ins[4], outs[4];
   for (int t = 0; t < 3; ++t) {
     ins[t] = span_of(src[t], 2);
     outs[t] = span_of(dst[t], 1);
   }
+  ins[3] = span_flat(kv_lens, B, 4);
   outs[2].hi += (uintptr_t)(s_pad - S);  // the last row's padding is written too
   outs[3] = span_flat(amax, 3 * B * H, 4);
   const char* on[4] = {dn[0], dn[1], dn[2], "amax"};
+  const char* in_names[4] = {sn[0], sn[1], sn[2], "kv_lens"};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 3; ++j)
-      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], sn[j]);
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], in_names[j]);
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], on[j]);
   }
@@ -293,13 +297,14 @@ lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax,
   }
   a.dst_sd_v = dst[2].stride[3];
   a.amax = amax;
+  a.kv_lens = kv_lens;
   a.B = (int)B; a.S = (int)S; a.H = (int)H;
   return launched(lsd::launch_cast_fp8(a, (hipStream_t)stream), "cast_qkv_fp8");
 }
 
 lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
-                        const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
-                        float softmax_scale, void* stream) {
+                        const float* k_amax, const float* v_amax, const int32_t* kv_lens, const lsd_view4* o,
+                        float* lse, float softmax_scale, void* stream) {
   lsd_status s;
   if ((s = check_view8("q8", q8, 3)) != LSD_OK) return s;
   if ((s = check_view8("k8", k8, 3)) != LSD_OK) return s;
@@ -323,13 +328,14 @@ lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view
     return fail(LSD_EINVAL, "amax arrays not 4-byte aligned");
   if (std::isinf(softmax_scale)) return fail(LSD_EINVAL, "softmax_scale is infinite");
   if (lse != nullptr && (uintptr_t)lse % 4 != 0) return fail(LSD_EINVAL, "lse not 4-byte aligned");
+  if (kv_lens != nullptr && (uintptr_t)kv_lens % 4 != 0) return fail(LSD_EINVAL, "kv_lens not 4-byte aligned");
   if (B * S_q * H == 0) return ok();
   Span vs = span_of(*v8, 1);
   if (S_kv > 0) vs.hi += (uintptr_t)((S_kv + 63) / 64 * 64 - S_kv);  // the padded tail of the last row
-  const Span ins[6] = {span_of(*q8, 1), span_of(*k8, 1), vs, span_flat(q_amax, B * H, 4),
-                       span_flat(k_amax, B * H, 4), span_flat(v_amax, B * H, 4)};
+  const Span ins[7] = {span_of(*q8, 1), span_of(*k8, 1), vs, span_flat(q_amax, B * H, 4),
+                       span_flat(k_amax, B * H, 4), span_flat(v_amax, B * H, 4), span_flat(kv_lens, B, 4)};
   const Span so = span_of(*o, 2), sl = span_flat(lse, B * H * S_q, 4);
-  for (int j = 0; j < 6; ++j) {
+  for (int j = 0; j < 7; ++j) {
     if (overlaps(so, ins[j])) return fail(LSD_EINVAL, "o overlaps an input");
     if (overlaps(sl, ins[j])) return fail(LSD_EINVAL, "lse overlaps an input");
   }
@@ -349,9 +355,10 @@ lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view
   a.o = (uint16_t*)o->data;
   a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2];
   a.lse = lse;
+  a.kv_lens = kv_lens;
   a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  return launched(lsd::launch_attn_fp8(a, (hipStream_t)stream), "attn_fwd_fp8");
+  return launched(lsd::launch_attn_fp8(a, (hipStream_t)stream), kv_lens ? "attn_fwd_fp8_masked" : "attn_fwd_fp8");
 }
 
 }  // namespace
@@ -551,13 +558,27 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
 extern "C" {
 
 lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream) {
-  return cast_qkv_fp8(src, dst, amax, stream);
+  return cast_qkv_fp8(src, dst, amax, nullptr, stream);
+}
+
+lsd_status lsd_cast_qkv_fp8_masked(const lsd_view4* src, const lsd_view4* dst, float* amax, const int32_t* kv_lens,
+                                   void* stream) {
+  if (kv_lens == nullptr) return fail(LSD_EINVAL, "null kv_lens");
+  return cast_qkv_fp8(src, dst, amax, kv_lens, stream);
 }
 
 lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
                             const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
                             float softmax_scale, void* stream) {
-  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o, lse, softmax_scale, stream);
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, nullptr, o, lse, softmax_scale, stream);
+}
+
+lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
+                                   const float* q_amax, const float* k_amax, const float* v_amax,
+                                   const int32_t* kv_lens, const lsd_view4* o, float* lse, float softmax_scale,
+                                   void* stream) {
+  if (kv_lens == nullptr) return fail(LSD_EINVAL, "null kv_lens");
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, kv_lens, o, lse, softmax_scale, stream);
 }
 
 lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,

@@ -151,7 +151,19 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int skv = a.S_kv;  // >= 1 here
+  // valid keys of this batch entry: all S_kv (>= 1 here), or the first
+  // kv_lens[b] (the key-only padding mask, clamped to [0, S_kv])
+  int skv = a.S_kv;
+  if (a.kv_lens != nullptr) skv = min(max(a.kv_lens[b], 0), a.S_kv);
+  if (skv == 0) {  // block-uniform: no keys for this (b, h): O = 0, LSE = -inf
+    for (int i = tid; i < kBlockM * (D / 8); i += kThreads) {
+      const int s = qt * kBlockM + i / (D / 8), c = i % (D / 8);
+      if (s >= a.S_q) continue;
+      *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = (u32x4){0u, 0u, 0u, 0u};
+      if (a.lse != nullptr && c == 0) a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
+    }
+    return;
+  }
   const int n_tiles = (skv + kBlockN - 1) / kBlockN;
   const float s_q = a.q_amax[b * a.H + h] / 448.0f;
   const float s_k = a.k_amax[b * a.H + h] / 448.0f;

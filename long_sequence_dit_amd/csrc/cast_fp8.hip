@@ -49,6 +49,13 @@ __device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
   return (uint32_t)v;
 }
 
+// Tokens of tensor t of batch entry b that count: all S for Q, the first
+// kv_lens[b] (clamped to [0, S]) for K and V under the key-length mask.
+__device__ inline int valid_tokens(const CastArgs& a, int t, int b) {
+  if (t == 0 || a.kv_lens == nullptr) return a.S;
+  return min(max(a.kv_lens[b], 0), a.S);
+}
+
 __global__ void amax_clear_kernel(float* amax, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) amax[i] = 0.0f;
@@ -59,8 +66,8 @@ __global__ void amax_clear_kernel(float* amax, int n) {
 // one word and measured slower, 256 by 2-5 %, 64 by 35 %), heads fastest across
 // waves (2 % faster than runs of one head fastest); a pass covers 4 tokens x 256 B
 // (16 lanes per token row of D = 128 channels).  The loads of 8 passes are
-// issued before any arithmetic; rows past S re-read row S - 1 (harmless for a
-// maximum), so the loop has no branches.
+// issued before any arithmetic; rows past the valid tokens re-read the last
+// valid row (harmless for a maximum), so the loop has no branches.
 constexpr int kAmaxRun = 512;
 
 __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs) {
@@ -74,6 +81,8 @@ __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs)
   const int run = (int)(rest % n_runs);
   const int b = (int)((rest / n_runs) % a.B);
   const int t = (int)(rest / ((int64_t)n_runs * a.B));
+  const int lim = valid_tokens(a, t, b);
+  if (run * kAmaxRun >= lim) return;  // no valid token in this run (wave-uniform)
   const uint16_t* base = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t] + 8 * (lane & 15);
   const int s0 = run * kAmaxRun + (lane >> 4);
   float m = 0.0f;
@@ -81,7 +90,7 @@ __global__ void __launch_bounds__(256) amax_kernel(const CastArgs a, int n_runs)
     u32x4 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + i0 + 4 * u, a.S - 1);
+      const int s = min(s0 + i0 + 4 * u, lim - 1);
       x[u] = __builtin_nontemporal_load((const u32x4*)(base + (int64_t)s * a.src_ss[t]));
     }
 #pragma unroll
@@ -126,7 +135,8 @@ __device__ inline float code_factor(const CastArgs& a, int t, int64_t bh) {
 // outputs take the flat pass below): one wave per (t in {0,1}, b, h, 64 tokens), heads fastest so that
 // waves running together read whole token rows; 16-byte bf16 vectors in,
 // 8-byte code vectors out.  All 16 loads of a lane are issued before any
-// conversion; rows past S re-read row S - 1 and are not stored.
+// conversion; rows past the valid tokens re-read the last valid row and are
+// not stored.
 __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_chunks) {
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -137,6 +147,8 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
   const int chunk = (int)(rest % n_chunks);
   const int b = (int)((rest / n_chunks) % a.B);
   const int t = (int)(rest / ((int64_t)n_chunks * a.B));
+  const int lim = valid_tokens(a, t, b);  // K codes past it are not written
+  if (chunk * kChunk >= lim) return;
   const float inv = code_factor(a, t, (int64_t)b * a.H + h);
   const uint16_t* src = a.src[t] + (int64_t)b * a.src_sb[t] + (int64_t)h * a.src_sh[t] + 8 * (lane & 15);
   uint8_t* dst = a.dst[t] + (int64_t)b * a.dst_sb[t] + (int64_t)h * a.dst_sh[t] + 8 * (lane & 15);
@@ -144,13 +156,13 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
   u32x4 x[kChunk / 4];
 #pragma unroll
   for (int u = 0; u < kChunk / 4; ++u) {
-    const int s = min(s0 + 4 * u, a.S - 1);
+    const int s = min(s0 + 4 * u, lim - 1);
     x[u] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[t]));
   }
 #pragma unroll
   for (int u = 0; u < kChunk / 4; ++u) {
     const int s = s0 + 4 * u;
-    if (s < a.S) {
+    if (s < lim) {
       u32x2 c;
       c[0] = pack4_fp8(bf16_lo(x[u][0]) * inv, bf16_hi(x[u][0]) * inv, bf16_lo(x[u][1]) * inv, bf16_hi(x[u][1]) * inv);
       c[1] = pack4_fp8(bf16_lo(x[u][2]) * inv, bf16_hi(x[u][2]) * inv, bf16_lo(x[u][3]) * inv, bf16_hi(x[u][3]) * inv);
@@ -168,7 +180,8 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(const CastArgs a, int n_c
 // LDS, each lane packing 16 tokens of each of its channels, measured 3-4 %
 // slower with 4, 8 or 16 waves per workgroup).  Rows are padded to a multiple
 // of 64 tokens: the last tile writes zero codes for tokens S .. the padded
-// end, and nothing past it.
+// end, and nothing past it; under the key-length mask the tokens from
+// kv_lens[b] on code as zero too.
 constexpr int kVTok = 256;
 constexpr int kVPitch = kVTok + 16;
 __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_chunks) {
@@ -180,6 +193,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   const float inv = inv_scale(a.amax[((int64_t)2 * a.B + b) * a.H + h]);
   const uint16_t* src = a.src[2] + (int64_t)b * a.src_sb[2] + (int64_t)h * a.src_sh[2];
   const int s0 = chunk * kVTok;
+  const int lim = valid_tokens(a, 2, b);  // tokens past it code as zero
   // Q's stored amax becomes its scale amax; the Q pass (an earlier launch)
   // has finished reading it
   if (chunk == 0 && threadIdx.x == 0) {
@@ -196,7 +210,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
     for (int i = 0; i < 4; ++i) {
       const int s = s0 + 64 * pass + 4 * g + i;
       x[pass][i] = (u32x4){0u, 0u, 0u, 0u};
-      if (s < a.S) x[pass][i] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[2] + 8 * c));
+      if (s < lim) x[pass][i] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)s * a.src_ss[2] + 8 * c));
     }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -220,7 +234,7 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   for (int p = tid; p < 128 * 16; p += 256) {
     const int d = p >> 4, q = p & 15;
     if (s0 + 16 * q >= s_end) continue;
-    const u32x4 val = *(const u32x4*)(tile + d * kVPitch + 16 * q);   // tokens >= S were loaded as 0
+    const u32x4 val = *(const u32x4*)(tile + d * kVPitch + 16 * q);   // tokens past lim were loaded as 0
     __builtin_nontemporal_store(val, (u32x4*)(dst + (int64_t)d * a.dst_sd_v + s0 + 16 * q));
   }
 }
@@ -246,7 +260,7 @@ __global__ void __launch_bounds__(256) amax_flat_kernel(const CastArgs a, int G)
   const int seg = blockIdx.x / G, g = blockIdx.x % G;  // seg = t * B + b
   const int t = seg / a.B, b = seg % a.B;
   for (int i = tid; i < a.H; i += 256) smax[i] = 0u;
-  const int64_t n = (int64_t)a.S * 16 * a.H;
+  const int64_t n = (int64_t)valid_tokens(a, t, b) * 16 * a.H;
   const int64_t stride = (int64_t)G * 256 * kU;
   const int64_t first = (int64_t)g * 256 * kU + tid;
   const u32x4* base = (const u32x4*)(a.src[t] + (int64_t)b * a.src_sb[t]);
@@ -291,7 +305,7 @@ __global__ void __launch_bounds__(256) quant_qk_flat_kernel(const CastArgs a, in
   const int tid = threadIdx.x;
   const int seg = blockIdx.x / G, g = blockIdx.x % G;  // seg = t * B + b, t in {0, 1}
   const int t = seg / a.B, b = seg % a.B;
-  const int64_t n = (int64_t)a.S * 16 * a.H;
+  const int64_t n = (int64_t)valid_tokens(a, t, b) * 16 * a.H;  // K codes past the valid tokens are not written
   const int64_t stride = (int64_t)G * 256 * kU;
   const int64_t first = (int64_t)g * 256 * kU + tid;
   const u32x4* src = (const u32x4*)(a.src[t] + (int64_t)b * a.src_sb[t]);

@@ -91,6 +91,10 @@ struct CastArgs {
   int64_t dst_sb[3], dst_ss[3], dst_sh[3];
   int64_t dst_sd_v;
   float* amax;  // [3, B, H]
+  // null, or per batch entry the number of valid K/V tokens (clamped to
+  // [0, S]): K and V amax over those only, V codes of the rest zero, K codes
+  // of the rest not written
+  const int32_t* kv_lens;
   int B, S, H;
 };
 hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t stream);
@@ -112,6 +116,7 @@ struct AttnFp8Args {
   uint16_t* o;
   int64_t o_sb, o_ss, o_sh;
   float* lse;  // [B, H, S_q], may be null
+  const int32_t* kv_lens;  // null, or valid keys per batch entry (clamped to [0, S_kv])
   int B, H, S_q, S_kv;
   float scale_log2;
 };

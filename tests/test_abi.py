@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
             "lsd_abi_version", "lsd_last_error"} <= set(syms)
     for s in syms:
         assert hasattr(L, s), f"{s} declared in lsd.h but not exported by liblsd.so"
-    assert L.lsd_abi_version() == 2
+    assert L.lsd_abi_version() == 3
 
 
 def view(addr, shape, stride=None):
@@ -313,6 +313,45 @@ def test_fp8_cast_and_attention_validation():
     assert r == LSD_EINVAL and "overlaps" in msg
     r, msg = attn8(q8, view8(BASE + 11 * GB, (B, S, H + 1, D), [S * (H + 1) * D, (H + 1) * D, D, 1]), v8, o)
     assert r == LSD_EINVAL and "k8 shape" in msg
+
+
+def test_fp8_masked_entry_points_validation():
+    """The key-length variants of the FP8 cast and attention: kv_lens must be
+    given, 4-byte aligned and clear of every output; the rest is checked as in
+    the unmasked calls (no launch is reached in these cases)."""
+    L = lsd.lib()
+    B, S, H, D = 2, 100, 3, 128
+    bf = [view(BASE + t * GB, (B, S, H, D)) for t in range(3)]
+    q8 = view8(BASE + 10 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    k8 = view8(BASE + 11 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    v8 = view8(BASE + 12 * GB, (B, S, H, D), [H * D * 128, 1, D * 128, 128])
+    amax = BASE + 13 * GB
+    lens = BASE + 14 * GB
+    o = view(BASE + 20 * GB, (B, S, H, D))
+
+    def cast(kl, dst=(q8, k8, v8)):
+        r = L.lsd_cast_qkv_fp8_masked((View4 * 3)(*bf), (View4 * 3)(*dst), ctypes.c_void_p(amax),
+                                      ctypes.c_void_p(kl) if kl else None, None)
+        return r, L.lsd_last_error().decode()
+
+    def attn8(kl, ov=o):
+        r = L.lsd_attn_fwd_fp8_masked(ctypes.byref(q8), ctypes.byref(k8), ctypes.byref(v8), ctypes.c_void_p(amax),
+                                      ctypes.c_void_p(amax + 64), ctypes.c_void_p(amax + 128),
+                                      ctypes.c_void_p(kl) if kl else None, ctypes.byref(ov), None,
+                                      ctypes.c_float(0.0), None)
+        return r, L.lsd_last_error().decode()
+
+    for fn in (cast, attn8):
+        r, msg = fn(0)
+        assert r == LSD_EINVAL and "null kv_lens" in msg
+        r, msg = fn(lens + 2)
+        assert r == LSD_EINVAL and "kv_lens not 4-byte aligned" in msg
+    r, msg = cast(BASE + 10 * GB + 16)                      # kv_lens inside q8's codes
+    assert r == LSD_EINVAL and "overlaps kv_lens" in msg
+    r, msg = attn8(BASE + 20 * GB + 16)                     # kv_lens inside o
+    assert r == LSD_EINVAL and "o overlaps an input" in msg
+    r, msg = cast(lens, dst=(q8, q8, v8))
+    assert r == LSD_EINVAL and "overlaps" in msg
 
 
 def test_attn_fwd_rejects_huge_kv_stride():

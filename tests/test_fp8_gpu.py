@@ -217,3 +217,93 @@ def test_key_counts_around_tile_halves_with_poisoned_padding(lo, n):
     assert t.isfinite(o.float()).all() and t.isfinite(lse).all()
     amax = np.stack([aq[0].cpu().numpy(), akv[1].cpu().numpy(), akv[2].cpu().numpy()])
     check_fp8(o, lse, codes(q8), hk, hv, amax, range(H), all_rows(S_q), f"fp8 keys [{lo}, {lo + n})")
+
+
+# ------------------------------------------------ key-length mask (FP8 path)
+
+NAN_BF16 = np.uint16(0x7FC1)
+MASK_LENS = [300, 1, 0, 127, 128, 129, 257, 64, 350, -3]   # the last two are clamped to 300 and 0
+
+
+def _lens_dev(lens):
+    t = torch()
+    return t.tensor(lens, dtype=t.int32, device="cuda")
+
+
+def _poisoned_qkv(lens, S, H, seed):
+    """Q, K, V [B, S, H, 128] whose K and V tokens from lens[b] on are NaN."""
+    B = len(lens)
+    q = synth.normal_bf16((B, S, H, 128), seed, 1)
+    k = synth.normal_bf16((B, S, H, 128), seed + 1, 1).copy()
+    v = synth.normal_bf16((B, S, H, 128), seed + 2, 1).copy()
+    for b, n in enumerate(lens):
+        k[b, max(0, min(n, S)):] = NAN_BF16
+        v[b, max(0, min(n, S)):] = NAN_BF16
+    return q, k, v
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "fused"])
+def test_masked_cast_bit_exact(layout):
+    """lsd_cast_qkv_fp8_masked: amax and the codes of Q (all tokens), K and V
+    (valid tokens) bit-exact against the oracle; V's codes of the padding up
+    to the padded row end zero; K's codes of the padding left as they were.
+    NaN in the padding; lengths across the 64-token chunks of the passes,
+    zero and out of range.  The contiguous layout takes the flat passes, the
+    fused [B, S, 3, H, D] views the per-head passes."""
+    note(f"fp8 masked cast ({layout})")
+    t = torch()
+    S, H = 300, 3
+    q, k, v = _poisoned_qkv(MASK_LENS, S, H, 120)
+    B = len(MASK_LENS)
+    if layout == "fused":
+        f = to_dev(np.stack([q, k, v], axis=2))
+        dq, dk, dv = f[:, :, 0], f[:, :, 1], f[:, :, 2]
+    else:
+        dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    out = lsd.fp8_buffers(B, S, H)
+    out[1].view(t.uint8).fill_(0x5A)                               # K padding must keep this
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(dq, dk, dv, out=out, kv_lens=_lens_dev(MASK_LENS))
+    t.cuda.synchronize()
+    eq8, ek8, ev8, eamax = fp8.cast_qkv(q, k, v, kv_lens=MASK_LENS)
+    assert np.array_equal(amax.cpu().numpy(), eamax), "amax"
+    assert np.array_equal(codes(q8), eq8), "q codes"
+    gk, gv = codes(k8), codes(v8)
+    for b, n in enumerate(MASK_LENS):
+        n = max(0, min(n, S))
+        assert np.array_equal(gk[b, :n], ek8[b, :n]), f"k codes b={b}"
+        assert np.all(gk[b, n:] == 0x5A), f"k padding written b={b}"
+    assert np.array_equal(gv, ev8), "v codes (padding zero)"
+    store = v8.as_strided((B, H, 128, (S + 63) // 64 * 64), (v8.stride(0), v8.stride(2), v8.stride(3), 1))
+    assert np.all(codes(store)[..., S:] == 0), "v row padding"
+
+
+@pytest.mark.parametrize("S,H", [(300, 2), (640, 2)])
+def test_masked_attention_within_fp8_contract(S, H):
+    """lsd_attn_fwd_fp8_masked on the masked cast of a padded batch: every
+    entry within the FP8 contract against the oracle's attention of its valid
+    keys (an entry without keys: O = 0, LSE = -inf); the output stays finite
+    although the K codes past the valid keys are NaN; with every length at
+    S_kv it is bit-identical to lsd_attn_fwd_fp8."""
+    note(f"fp8 masked attention S={S} H={H}")
+    t = torch()
+    lens = [S, 1, 0, 127, 128, 129, 257, 64, S + 50, -3]
+    q, k, v = _poisoned_qkv(lens, S, H, 130)
+    ld = _lens_dev(lens)
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(to_dev(q), to_dev(k), to_dev(v), kv_lens=ld)
+    for b, n in enumerate(lens):
+        k8.view(t.uint8)[b, max(0, min(n, S)):] = 0x7F                            # E4M3 NaN past the valid keys
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2], kv_lens=ld)
+    t.cuda.synchronize()
+    assert t.isfinite(o.float()).all()
+    cq, ck, cv, am = codes(q8), codes(k8), codes(v8), amax.cpu().numpy()
+    for b, n in enumerate(lens):
+        n = max(0, min(n, S))
+        check_fp8(o[b:b + 1], lse[b:b + 1], cq[b:b + 1], ck[b:b + 1, :n], cv[b:b + 1, :n], am[:, b:b + 1],
+                  range(H), all_rows(S), f"fp8 masked b={b} len={n}")
+    full = _lens_dev([S] * len(lens))
+    qa, ka, va = (to_dev(synth.normal_bf16((len(lens), S, H, 128), 140 + i, 1)) for i in range(3))
+    q8a, k8a, v8a, ama = lsd.cast_qkv_fp8(qa, ka, va)
+    o1, l1 = lsd.attn_fwd_fp8(q8a, k8a, v8a, ama[0], ama[1], ama[2])
+    o2, l2 = lsd.attn_fwd_fp8(q8a, k8a, v8a, ama[0], ama[1], ama[2], kv_lens=full)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
