@@ -117,6 +117,33 @@ def test_ltx2_scale_fp8():
     check_fp8(o, lse, hq, hk, hv, eamax, range(32), lambda b, h: sample_rows(24576, 300 + h), "LTX-2 fp8")
 
 
+def test_ltx2_scale_fp8_key_padding_mask():
+    """Full LTX-2 on the FP8 path with the key-length mask: 21,000 of 24,576
+    keys valid, NaN padding; the masked cast bit-exact against the oracle's
+    (K and V scales from the valid tokens, V padding codes zero), attention
+    within the FP8 contract against the oracle over the valid keys."""
+    note("full LTX-2 on the FP8 path with a key-only mask: 21,000 of 24,576 keys valid, NaN padding")
+    from test_fp8_gpu import check_fp8, codes
+    from oracle import fp8 as ofp8
+    t = torch()
+    q, k, v = synth.ltx2_qkv()
+    n = 21_000
+    k = k.copy()
+    v = v.copy()
+    k[:, n:] = 0x7FC1
+    v[:, n:] = 0x7FC1
+    lens = t.tensor([n], dtype=t.int32, device="cuda")
+    q8, k8, v8, amax = lsd.cast_qkv_fp8(to_dev(q), to_dev(k), to_dev(v), kv_lens=lens)
+    o, lse = lsd.attn_fwd_fp8(q8, k8, v8, amax[0], amax[1], amax[2], kv_lens=lens)
+    t.cuda.synchronize()
+    eq8, ek8, ev8, eamax = ofp8.cast_qkv(q, k, v, kv_lens=[n])
+    hq, hk, hv = codes(q8), codes(k8)[:, :n], codes(v8)
+    assert np.array_equal(amax.cpu().numpy(), eamax) and np.array_equal(hq, eq8)
+    assert np.array_equal(hk, ek8[:, :n]) and np.array_equal(hv, ev8)
+    check_fp8(o, lse, hq, hk, hv[:, :n], eamax, range(32), lambda b, h: sample_rows(24576, 500 + h),
+              "LTX-2 fp8 masked")
+
+
 def test_wan_ulysses_share_relayout_then_attention():
     note("full Wan Ulysses share: fused QKV [2,75600,3,40,128] -> rank slices, P=4")
     t = torch()
