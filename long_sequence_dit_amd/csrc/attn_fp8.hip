@@ -7,7 +7,10 @@
 // ("Scaling Video Generation Across NVL72 rack with TensorRT-LLM", "Ulysses
 // Parallelism > Fused vs. unfused QKV all-to-all": FP8 inputs for the
 // attention kernel, produced by one cast of the stacked QKV; "The Scaling
-// Challenge in Video Generation": dense, unmasked attention).
+// Challenge in Video Generation": dense, unmasked attention).  With a key
+// count per batch entry (the key-only padding mask of "How 8 GPUs split
+// tokens: what LTX-2's sequence-parallel all2all moves", "Data flow") an
+// entry attends its first kv_lens[b] keys only.
 //
 // The structure follows the bf16 kernel (8 waves, 256 query rows per
 // workgroup, key tiles double-buffered in LDS, the two waves of a SIMD

@@ -15,6 +15,9 @@
 // block scales (q_scale_amax; heads with a zero amax keep amax_q).
 // Q and K keep their (B, S, H, D) layout; V is written transposed, keys
 // contiguous per (b, h, d), which is the operand layout of the PV product.
+// With a key count per batch entry (the key-only padding mask), K's and V's
+// tokens from kv_lens[b] on are padding: they take no part in the amax, V's
+// codes there are zero and K's are not written.
 //
 // Four launches on the caller's stream: clear amax, reduce it (integer max
 // on the float bits of non-negative values: order-independent, so the result
