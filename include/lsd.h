@@ -14,6 +14,8 @@
  *   lsd_attn_fwd_fp8          attention on the FP8 inputs
  *   lsd_cast_qkv_fp8_masked   the cast with a per-batch key count
  *   lsd_attn_fwd_fp8_masked   FP8 attention with a per-batch key count
+ *   lsd_attn_fwd_fp8_accumulate  FP8 attention against one K/V block, merged
+ *                             in place into a running (O, LSE) (Ring step)
  *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
  *                             after attention)
  *
@@ -57,7 +59,8 @@ extern "C" {
 /* 2: lsd_cast_qkv_fp8 stores Q's scale amax (a power-of-two logit factor)
  *    in place of Q's plain amax; signatures unchanged from 1.
  * 3: adds lsd_cast_qkv_fp8_masked and lsd_attn_fwd_fp8_masked (the key-length
- *    mask on the FP8 path); earlier entry points unchanged. */
+ *    mask on the FP8 path) and lsd_attn_fwd_fp8_accumulate (the fused Ring
+ *    step on FP8 inputs); earlier entry points unchanged. */
 #define LSD_ABI_VERSION 3
 
 typedef enum lsd_status {
@@ -295,6 +298,35 @@ lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, con
                                    const float* q_amax, const float* k_amax, const float* v_amax,
                                    const int32_t* kv_lens, const lsd_view4* o, float* lse, float softmax_scale,
                                    void* stream);
+
+/*
+ * One Ring step on FP8 inputs with the merge folded in: lsd_attn_fwd_fp8 of q8
+ * against one key/value block (its codes and scales as the FP8 cast of that
+ * block writes them), merged into a running result in place, exactly as
+ * lsd_attn_fwd_accumulate merges (same rules for o_acc, lse_acc, o, kv_lens
+ * and an empty block).  Defined by "Scaling Video Generation Across NVL72 rack
+ * with TensorRT-LLM", "Context Parallelism > Ring Attention" (each arriving
+ * block's partial result merged into the running output with the fp32
+ * online-softmax recurrence) and "Limitations and Future Work" (the combine
+ * folded into the attention kernel), on the FP8 inputs of "Ulysses
+ * Parallelism > Fused vs. unfused QKV all-to-all".
+ *
+ *   q8, k8, v8, q_amax, k_amax, v_amax  as for lsd_attn_fwd_fp8 (k8, v8 and
+ *            their scales: this step's block)
+ *   kv_lens  NULL, or this block's valid keys per batch entry (as for
+ *            lsd_attn_fwd_fp8_masked)
+ *   o_acc    float32 [B, S_q, H, D] contiguous, 16-byte aligned: read, written
+ *   lse_acc  float32 [B, H, S_q] contiguous: read, written
+ *   o        (B, S_q, H, D) bf16, written if non-NULL (the updated running
+ *            output in bf16)
+ *
+ * The block's own result carries the FP8 error of lsd_attn_fwd_fp8; the merge
+ * is the float32 arithmetic of lsd_attn_fwd_accumulate.
+ */
+lsd_status lsd_attn_fwd_fp8_accumulate(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
+                                       const float* q_amax, const float* k_amax, const float* v_amax,
+                                       const int32_t* kv_lens, float* o_acc, float* lse_acc, const lsd_view4* o,
+                                       float softmax_scale, void* stream);
 
 /*
  * Ulysses sequence-major -> head-major relayout for one destination rank.

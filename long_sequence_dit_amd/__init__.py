@@ -70,6 +70,10 @@ def lib():
         L.lsd_attn_fwd_fp8_masked.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, P(View4), ctypes.c_void_p,
                                               ctypes.c_float, ctypes.c_void_p]
+        L.lsd_attn_fwd_fp8_accumulate.restype = ctypes.c_int
+        L.lsd_attn_fwd_fp8_accumulate.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, P(View4), ctypes.c_float, ctypes.c_void_p]
         L.lsd_relayout_head_to_seq.restype = ctypes.c_int
         L.lsd_relayout_head_to_seq.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(View4),
                                                P(View4), ctypes.c_void_p]
@@ -308,6 +312,29 @@ def attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o=None, lse=None, scale: Op
                                            _lens_ptr(kv_lens, B), ctypes.byref(ov), lp, sc, _stream(q8))
         _check(st, "lsd_attn_fwd_fp8_masked")
     return (o, lse) if lse is not None else o
+
+
+def attn_fwd_fp8_accumulate(q8, k8, v8, q_amax, k_amax, v_amax, o_acc, lse_acc, o=None,
+                            scale: Optional[float] = None, kv_lens=None):
+    """One Ring step on FP8 inputs: FP8 attention of q8 against this K/V block
+    (codes and scales of the block's cast), merged in place into the running
+    float32 ``o_acc`` (B, S_q, H, D) and ``lse_acc`` (B, H, S_q); start with
+    lse_acc = -inf.  ``o`` (bf16), if given, receives the updated result.
+    ``kv_lens`` is the block's key-length mask.  Returns o."""
+    B, S_q, H, D = q8.shape
+    if o_acc is None or lse_acc is None:
+        raise ValueError("attn_fwd_fp8_accumulate: o_acc and lse_acc are required")
+    qv, kv, vv = _view8(q8, "q8"), _view8(k8, "k8"), _view8(v8, "v8")
+    ov = _view(o, "o") if o is not None else None
+    pq, pk, pv = (_f32_ptr(x, n, (B, H)) for x, n in ((q_amax, "q_amax"), (k_amax, "k_amax"), (v_amax, "v_amax")))
+    pa = _f32_ptr(o_acc, "o_acc", (B, S_q, H, D))
+    pl = _f32_ptr(lse_acc, "lse_acc", (B, H, S_q))
+    st = lib().lsd_attn_fwd_fp8_accumulate(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), pq, pk, pv,
+                                           _lens_ptr(kv_lens, B), pa, pl,
+                                           ctypes.byref(ov) if ov is not None else None,
+                                           ctypes.c_float(0.0 if scale is None else float(scale)), _stream(q8))
+    _check(st, "lsd_attn_fwd_fp8_accumulate")
+    return o
 
 
 def relayout_seq_to_head(src: Sequence[Sequence], P: int, rank: int, dst: Optional[List] = None):

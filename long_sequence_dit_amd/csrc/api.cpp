@@ -304,20 +304,25 @@ lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax,
 
 lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
                         const float* k_amax, const float* v_amax, const int32_t* kv_lens, const lsd_view4* o,
-                        float* lse, float softmax_scale, void* stream) {
+                        float* lse, float* o_acc, float* lse_acc, bool acc, float softmax_scale, void* stream) {
   lsd_status s;
   if ((s = check_view8("q8", q8, 3)) != LSD_OK) return s;
   if ((s = check_view8("k8", k8, 3)) != LSD_OK) return s;
   if ((s = check_view8("v8 (transposed)", v8, 1)) != LSD_OK) return s;
-  if ((s = check_view("o", o)) != LSD_OK) return s;
+  if ((!acc || o != nullptr) && (s = check_view("o", o)) != LSD_OK) return s;
   const int64_t B = q8->shape[0], S_q = q8->shape[1], H = q8->shape[2], D = q8->shape[3];
   const int64_t S_kv = k8->shape[1];
   if (k8->shape[0] != B || k8->shape[2] != H || k8->shape[3] != D)
     return fail(LSD_EINVAL, "k8 shape does not match q8 (B=%lld, H=%lld, D=%lld)", (long long)B, (long long)H,
                 (long long)D);
   if (!same_shape(*v8, *k8)) return fail(LSD_EINVAL, "v8 shape must equal k8 shape (B, S_kv, H, D)");
-  if (!same_shape(*o, *q8)) return fail(LSD_EINVAL, "o shape must equal q8 shape (B, S_q, H, D)");
+  if (o != nullptr && !same_shape(*o, *q8)) return fail(LSD_EINVAL, "o shape must equal q8 shape (B, S_q, H, D)");
   if (D != 128) return fail(LSD_EUNSUPPORTED, "FP8 path: head dim D=%lld unsupported (128)", (long long)D);
+  if (acc) {
+    if (o_acc == nullptr || lse_acc == nullptr) return fail(LSD_EINVAL, "null o_acc or lse_acc");
+    if ((uintptr_t)o_acc % 16 != 0) return fail(LSD_EINVAL, "o_acc not 16-byte aligned");
+    if ((uintptr_t)lse_acc % 4 != 0) return fail(LSD_EINVAL, "lse_acc not 4-byte aligned");
+  }
   if (k8->stride[1] >= (int64_t(1) << 24) || v8->stride[3] >= (int64_t(1) << 24))
     return fail(LSD_EUNSUPPORTED, "k8 sequence stride / v8 row pitch must be below 2^24 bytes");
   if (S_kv > 0 && v8->stride[3] < (S_kv + 63) / 64 * 64)
@@ -334,12 +339,17 @@ lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view
   if (S_kv > 0) vs.hi += (uintptr_t)((S_kv + 63) / 64 * 64 - S_kv);  // the padded tail of the last row
   const Span ins[7] = {span_of(*q8, 1), span_of(*k8, 1), vs, span_flat(q_amax, B * H, 4),
                        span_flat(k_amax, B * H, 4), span_flat(v_amax, B * H, 4), span_flat(kv_lens, B, 4)};
-  const Span so = span_of(*o, 2), sl = span_flat(lse, B * H * S_q, 4);
-  for (int j = 0; j < 7; ++j) {
-    if (overlaps(so, ins[j])) return fail(LSD_EINVAL, "o overlaps an input");
-    if (overlaps(sl, ins[j])) return fail(LSD_EINVAL, "lse overlaps an input");
+  const Span none = span_flat(nullptr, 0, 1);
+  const Span so = o != nullptr ? span_of(*o, 2) : none, sl = span_flat(lse, B * H * S_q, 4);
+  const Span soa = span_flat(o_acc, B * S_q * H * D, 4), sla = span_flat(lse_acc, B * H * S_q, 4);
+  const Span outs[4] = {so, sl, soa, sla};
+  const char* onames[4] = {"o", "lse", "o_acc", "lse_acc"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps an input", onames[i]);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", onames[i], onames[j]);
   }
-  if (overlaps(sl, so)) return fail(LSD_EINVAL, "lse overlaps o");
   if ((s = check_device()) != LSD_OK) return s;
 
   const float scale = (softmax_scale > 0.0f) ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
@@ -352,13 +362,16 @@ lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view
   a.k_sb = k8->stride[0]; a.k_ss = k8->stride[1]; a.k_sh = k8->stride[2];
   a.vt_sb = v8->stride[0]; a.vt_sh = v8->stride[2]; a.vt_sd = v8->stride[3];
   a.q_amax = q_amax; a.k_amax = k_amax; a.v_amax = v_amax;
-  a.o = (uint16_t*)o->data;
-  a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2];
-  a.lse = lse;
+  a.o = o != nullptr ? (uint16_t*)o->data : nullptr;
+  if (o != nullptr) { a.o_sb = o->stride[0]; a.o_ss = o->stride[1]; a.o_sh = o->stride[2]; }
+  a.lse = acc ? nullptr : lse;
   a.kv_lens = kv_lens;
+  a.o_acc = acc ? o_acc : nullptr;
+  a.lse_acc = acc ? lse_acc : nullptr;
   a.B = (int)B; a.H = (int)H; a.S_q = (int)S_q; a.S_kv = (int)S_kv;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  return launched(lsd::launch_attn_fp8(a, (hipStream_t)stream), kv_lens ? "attn_fwd_fp8_masked" : "attn_fwd_fp8");
+  return launched(lsd::launch_attn_fp8(a, (hipStream_t)stream),
+                  acc ? "attn_fwd_fp8_accumulate" : (kv_lens ? "attn_fwd_fp8_masked" : "attn_fwd_fp8"));
 }
 
 }  // namespace
@@ -570,7 +583,8 @@ lsd_status lsd_cast_qkv_fp8_masked(const lsd_view4* src, const lsd_view4* dst, f
 lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
                             const float* k_amax, const float* v_amax, const lsd_view4* o, float* lse,
                             float softmax_scale, void* stream) {
-  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, nullptr, o, lse, softmax_scale, stream);
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, nullptr, o, lse, nullptr, nullptr, false, softmax_scale,
+                      stream);
 }
 
 lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
@@ -578,7 +592,16 @@ lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, con
                                    const int32_t* kv_lens, const lsd_view4* o, float* lse, float softmax_scale,
                                    void* stream) {
   if (kv_lens == nullptr) return fail(LSD_EINVAL, "null kv_lens");
-  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, kv_lens, o, lse, softmax_scale, stream);
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, kv_lens, o, lse, nullptr, nullptr, false, softmax_scale,
+                      stream);
+}
+
+lsd_status lsd_attn_fwd_fp8_accumulate(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
+                                       const float* q_amax, const float* k_amax, const float* v_amax,
+                                       const int32_t* kv_lens, float* o_acc, float* lse_acc, const lsd_view4* o,
+                                       float softmax_scale, void* stream) {
+  return attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, kv_lens, o, nullptr, o_acc, lse_acc, true, softmax_scale,
+                      stream);
 }
 
 lsd_status lsd_relayout_seq_to_head(int n_tensors, int P, int rank, const lsd_view4* src, const lsd_view4* dst,

@@ -72,6 +72,9 @@ constexpr int kLdsV = D * kRowV;           // bytes per V^T buffer
 constexpr int kRowO = D + 4;               // output staging pitch (bf16 elements)
 constexpr int kLdsO = kWaves * 32 * kRowO * 2;
 constexpr int kLds = (2 * (kLdsK + kLdsV) > kLdsO) ? 2 * (kLdsK + kLdsV) : kLdsO;
+constexpr int kRowA = D + 4;                // fp32 staging pitch of the accumulate epilogue
+constexpr int kLdsA = kWaves * (32 * kRowA + 32) * 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
   bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
@@ -132,8 +135,12 @@ __device__ inline int k_lds_row(int kk) {
   return (kk & ~31) + 8 * ((x & 15) >> 2) + 4 * (x >> 4) + (x & 3);
 }
 
+// kAcc: the fused Ring step - this block's result is merged into the running
+// (o_acc, lse_acc) in the epilogue, as in the bf16 kernel.
+template <bool kAcc>
 __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  constexpr int kSmem = (kAcc && kLdsA > kLds) ? kLdsA : kLds;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   uint8_t* Ks = smem;               // [2][64][kRowK] bytes, rows permuted
   uint8_t* Vs = smem + 2 * kLdsK;   // [2][D][kRowV] bytes, V^T
 
@@ -158,12 +165,26 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   // kv_lens[b] (the key-only padding mask, clamped to [0, S_kv])
   int skv = a.S_kv;
   if (a.kv_lens != nullptr) skv = min(max(a.kv_lens[b], 0), a.S_kv);
-  if (skv == 0) {  // block-uniform: no keys for this (b, h): O = 0, LSE = -inf
+  if (skv == 0) {  // block-uniform: no keys for this (b, h)
+    // O = 0, LSE = -inf; in accumulate mode the running result stays and O,
+    // if requested, is that result in bf16 (0 where there is none)
     for (int i = tid; i < kBlockM * (D / 8); i += kThreads) {
       const int s = qt * kBlockM + i / (D / 8), c = i % (D / 8);
       if (s >= a.S_q) continue;
-      *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = (u32x4){0u, 0u, 0u, 0u};
-      if (a.lse != nullptr && c == 0) a.lse[((int64_t)b * a.H + h) * a.S_q + s] = -INFINITY;
+      const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + s;
+      u32x4 out = {0u, 0u, 0u, 0u};
+      if constexpr (kAcc) {
+        if (a.o == nullptr) continue;
+        if (a.lse_acc[lrow] != -INFINITY) {
+          const f32x4* src = (const f32x4*)(a.o_acc + (((int64_t)b * a.S_q + s) * a.H + h) * D + 8 * c);
+          const f32x4 x0 = src[0], x1 = src[1];
+          out = (u32x4){pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]), pack_bf16(x1[0], x1[1]),
+                        pack_bf16(x1[2], x1[3])};
+        }
+      } else if (a.lse != nullptr && c == 0) {
+        a.lse[lrow] = -INFINITY;
+      }
+      *(u32x4*)(a.o + (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + 8 * c) = out;
     }
     return;
   }
@@ -461,6 +482,61 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
   // ---- epilogue: O = s_v O^T / l, LSE = ln 2 (m + log2 l), O staged through LDS
   const float l_tot = partner_sum(l_run);
   const float osc = s_v / l_tot;
+  constexpr float kLn2 = 0.69314718055994530942f;
+  if constexpr (kAcc) {
+    // Merge with the running result of earlier key blocks (exact LSE merge,
+    // fp32): with M = max(LSE_acc, LSE_blk) and w = exp(LSE - M),
+    //   O_acc <- (w_acc O_acc + w_blk O_blk) / (w_acc + w_blk),
+    //   LSE_acc <- M + ln(w_acc + w_blk).
+    // LSE_blk is finite (the block has keys), so M is; rows with no history
+    // (LSE_acc = -inf) get w_acc = 0 and their O_acc is not read.  The
+    // weighted block rows go through LDS (free once every wave has left the
+    // loop), so the fp32 running O is read and written in whole 512-byte rows.
+    const int64_t lrow = ((int64_t)b * a.H + h) * a.S_q + qrow;
+    const float lse_b = (m_run + __log2f(l_tot)) * kLn2;
+    const float lse_a = qvalid ? a.lse_acc[lrow] : -INFINITY;
+    const float mx = fmaxf(lse_a, lse_b);
+    const float wa = expf(lse_a - mx);
+    const float wb = expf(lse_b - mx);
+    const float rs = 1.0f / (wa + wb);
+    const float ca = wa * rs, cb = wb * rs * osc;
+    if (hh == 0 && qvalid) a.lse_acc[lrow] = mx + logf(wa + wb);
+    __syncthreads();
+    float* Aw = (float*)smem + wave * (32 * kRowA + 32);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 w = {oacc[db][4 * g + 0] * cb, oacc[db][4 * g + 1] * cb, oacc[db][4 * g + 2] * cb,
+                         oacc[db][4 * g + 3] * cb};
+        *(f32x4*)(Aw + l32 * kRowA + 32 * db + 8 * g + 4 * hh) = w;
+      }
+    if (hh == 0) Aw[32 * kRowA + l32] = ca;
+    __syncthreads();
+    // lane -> (row, 16-byte chunk of the row): 2 rows per pass
+    constexpr int kCPRA = D / 4;
+    constexpr int kRowsPerPassA = 64 / kCPRA;
+    const int cha = lane % kCPRA;
+    const int row_base_a = qt * kBlockM + wave * 32;
+#pragma unroll 4
+    for (int r = lane / kCPRA; r < 32; r += kRowsPerPassA) {
+      const int row = row_base_a + r;
+      if (row >= a.S_q) break;  // rows past S_q only at the end of the wave's range
+      const float car = Aw[32 * kRowA + r];
+      f32x4 nv = *(const f32x4*)(Aw + r * kRowA + 4 * cha);
+      float* gp = a.o_acc + (((int64_t)b * a.S_q + row) * a.H + h) * D + 4 * cha;
+      if (car > 0.0f) {  // history exists (w_acc > 0): O_acc holds data
+        const f32x4 prev = *(const f32x4*)gp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nv[e] = __builtin_fmaf(prev[e], car, nv[e]);
+      }
+      *(f32x4*)gp = nv;
+      if (a.o != nullptr)
+        *(u32x2*)(a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh + 4 * cha) =
+            (u32x2){pack_bf16(nv[0], nv[1]), pack_bf16(nv[2], nv[3])};
+    }
+    return;
+  }
   __syncthreads();
   uint16_t* Ow = (uint16_t*)smem + wave * 32 * kRowO;
 #pragma unroll
@@ -472,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) attn_fp8_kernel(const AttnFp8Args a,
       *(u32x2*)(Ow + l32 * kRowO + 32 * db + 8 * g + 4 * hh) = w;
     }
   if (a.lse != nullptr && hh == 0 && qvalid)
-    a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    a.lse[((int64_t)b * a.H + h) * a.S_q + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   constexpr int kCPR = D / 8;
   constexpr int kRowsPerPass = 64 / kCPR;
   const int ch = lane % kCPR;
@@ -505,7 +581,7 @@ __global__ void attn_fp8_empty_kernel(const AttnFp8Args a) {
 }  // namespace
 
 hipError_t launch_attn_fp8(const AttnFp8Args& a, hipStream_t stream) {
-  if (a.S_kv == 0) {
+  if (a.S_kv == 0 && a.o_acc == nullptr) {
     const int64_t n = (int64_t)a.B * a.S_q * a.H * (D / 8);
     const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
     hipLaunchKernelGGL(attn_fp8_empty_kernel, dim3(blocks), dim3(256), 0, stream, a);
@@ -514,7 +590,10 @@ hipError_t launch_attn_fp8(const AttnFp8Args& a, hipStream_t stream) {
   const int n_qtiles = (a.S_q + kBlockM - 1) / kBlockM;
   const int64_t nblk = (int64_t)n_qtiles * a.H * a.B;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+  if (a.o_acc != nullptr)  // accumulate mode (an empty block too: its rows keep the running result)
+    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
+  else
+    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, a, n_qtiles);
   return hipGetLastError();
 }
 

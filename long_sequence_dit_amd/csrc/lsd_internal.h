@@ -117,6 +117,10 @@ struct AttnFp8Args {
   int64_t o_sb, o_ss, o_sh;
   float* lse;  // [B, H, S_q], may be null
   const int32_t* kv_lens;  // null, or valid keys per batch entry (clamped to [0, S_kv])
+  // accumulate mode (both non-null): running fp32 O [B, S_q, H, D] and LSE
+  // [B, H, S_q], merged in place; o may then be null
+  float* o_acc;
+  float* lse_acc;
   int B, H, S_q, S_kv;
   float scale_log2;
 };

@@ -177,6 +177,14 @@ def attention_fp8(q8, k8, v8, q_amax, k_amax, v_amax, scale=None, kv_lens=None):
                          kv_lens=kv_lens)
 
 
+def attention_fp8_accumulate(o_acc, lse_acc, q8, k8, v8, q_amax, k_amax, v_amax, scale=None, kv_lens=None):
+    """One Ring step on FP8 inputs: ``ref.attention_accumulate`` of the
+    dequantised q against this key/value block (its codes and per-(batch,
+    head) scales), merged into the running (O_acc, LSE_acc); float64."""
+    return ref.attention_accumulate(o_acc, lse_acc, dequantize(q8, q_amax), dequantize(k8, k_amax),
+                                    dequantize(v8, v_amax), scale, kv_lens)
+
+
 def attention_fp8_rows(q8, k8, v8, q_amax, k_amax, v_amax, b: int, h: int, rows, scale=None, kv_len=None):
     """``attention_fp8`` for selected query rows of one (batch, head), over
     the first ``kv_len`` keys (all of them by default)."""

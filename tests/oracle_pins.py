@@ -650,6 +650,34 @@ def pin_fp8_key_lengths():
                                                                                        atol=1e-12)
 
 
+def pin_fp8_ring_steps():
+    """Ring steps on FP8 inputs: three key/value blocks, each cast with its own
+    scales, streamed into a running result from LSE = -inf, give the attention
+    of the dequantised query against all dequantised blocks together (the
+    exact merge); an empty block leaves the result unchanged."""
+    from oracle import fp8
+    B, S_q, H, D = 1, 30, 2, 64
+    q = _rand((B, S_q, H, D), 71)
+    q8, _, _, aq = fp8.cast_qkv(q, q, q)
+    blocks = []
+    for i, n in enumerate((17, 40, 9)):
+        k = synth.f32_to_bf16_bits(_dec(_rand((B, n, H, D), 72 + i)).astype(np.float32) * (1.0 + i))
+        v = _rand((B, n, H, D), 80 + i)
+        _, k8, v8, a = fp8.cast_qkv(k, k, v)
+        blocks.append((k8, v8, a[1], a[2]))
+    o = np.zeros((B, S_q, H, D))
+    lse = np.full((B, H, S_q), -np.inf)
+    for k8, v8, ak, av in blocks:
+        o, lse = fp8.attention_fp8_accumulate(o, lse, q8, k8, v8, aq[0], ak, av, scale=0.1)
+    K = np.concatenate([fp8.dequantize(k8, ak) for k8, _, ak, _ in blocks], axis=1)
+    V = np.concatenate([fp8.dequantize(v8, av) for _, v8, _, av in blocks], axis=1)
+    O, L = ref.attention(fp8.dequantize(q8, aq[0]), K, V, scale=0.1)
+    assert np.allclose(o, O, rtol=0, atol=1e-12) and np.allclose(lse, L, rtol=0, atol=1e-12)
+    k8, v8, ak, av = blocks[0]
+    o2, l2 = fp8.attention_fp8_accumulate(o, lse, q8, k8[:, :0], v8[:, :0], aq[0], ak, av, scale=0.1)
+    assert np.array_equal(o2, o) and np.array_equal(l2, lse)
+
+
 FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_q_scale, pin_fp8_attention,
-            pin_fp8_key_lengths]
+            pin_fp8_key_lengths, pin_fp8_ring_steps]
 ALL_PINS = ALL_PINS + FP8_PINS

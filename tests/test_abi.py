@@ -354,6 +354,38 @@ def test_fp8_masked_entry_points_validation():
     assert r == LSD_EINVAL and "overlaps" in msg
 
 
+def test_fp8_accumulate_validation():
+    """The FP8 Ring step: o_acc and lse_acc must be given and aligned, and no
+    output (o_acc, lse_acc, o) may overlap an input or another output."""
+    L = lsd.lib()
+    B, S, H, D = 2, 100, 3, 128
+    q8 = view8(BASE + 10 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    k8 = view8(BASE + 11 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    v8 = view8(BASE + 12 * GB, (B, S, H, D), [H * D * 128, 1, D * 128, 128])
+    amax = BASE + 13 * GB
+    o_acc, lse_acc = BASE + 15 * GB, BASE + 16 * GB
+
+    def acc(oa, la, o=None):
+        r = L.lsd_attn_fwd_fp8_accumulate(ctypes.byref(q8), ctypes.byref(k8), ctypes.byref(v8), ctypes.c_void_p(amax),
+                                          ctypes.c_void_p(amax + 64), ctypes.c_void_p(amax + 128), None,
+                                          ctypes.c_void_p(oa) if oa else None, ctypes.c_void_p(la) if la else None,
+                                          None if o is None else ctypes.byref(o), ctypes.c_float(0.0), None)
+        return r, L.lsd_last_error().decode()
+
+    r, msg = acc(0, lse_acc)
+    assert r == LSD_EINVAL and "null o_acc or lse_acc" in msg
+    r, msg = acc(o_acc + 4, lse_acc)
+    assert r == LSD_EINVAL and "o_acc not 16-byte aligned" in msg
+    r, msg = acc(o_acc, lse_acc + 2)
+    assert r == LSD_EINVAL and "lse_acc not 4-byte aligned" in msg
+    r, msg = acc(BASE + 10 * GB + 64, lse_acc)
+    assert r == LSD_EINVAL and "o_acc overlaps an input" in msg
+    r, msg = acc(o_acc, o_acc + 256)
+    assert r == LSD_EINVAL and "lse_acc overlaps o_acc" in msg
+    r, msg = acc(o_acc, lse_acc, view(o_acc + 1024, (B, S, H, D)))
+    assert r == LSD_EINVAL and "overlaps o" in msg
+
+
 def test_attn_fwd_rejects_huge_kv_stride():
     q, k, v, o = good4()
     k = view(BASE + GB, (1, 256, 2, 64), [256 * (1 << 24), 1 << 24, 64, 1])

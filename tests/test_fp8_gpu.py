@@ -307,3 +307,67 @@ def test_masked_attention_within_fp8_contract(S, H):
     o2, l2 = lsd.attn_fwd_fp8(q8a, k8a, v8a, ama[0], ama[1], ama[2], kv_lens=full)
     t.cuda.synchronize()
     assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
+
+
+# ------------------------------------------------ fused Ring step (FP8 path)
+
+def test_fp8_ring_steps_within_contract():
+    """lsd_attn_fwd_fp8_accumulate over four K/V blocks (each cast with its
+    own scales; one with a key-length mask, one whose every entry is empty),
+    each step checked from the GPU's own prior state: the merged O within the
+    FP8 bound of the block's result weighted by the block's share
+    w_b / (w_acc + w_b) (plus float32 merge rounding), the LSE within 1e-3,
+    an empty block leaving the running result bit-identical, and the bf16
+    output the running O rounded."""
+    note("fp8 fused Ring steps")
+    t = torch()
+    B, S_q, H = 2, 200, 2
+    sc = ref._default_scale(128, None)
+    q = synth.normal_bf16((B, S_q, H, 128), 150, 1)
+    dq = to_dev(q)
+    q8, _, _, aq = lsd.cast_qkv_fp8(dq, dq, dq)
+    cq, am_q = codes(q8), aq[0].cpu().numpy()
+    o_acc = t.zeros((B, S_q, H, 128), dtype=t.float32, device="cuda")
+    lse_acc = t.full((B, H, S_q), float("-inf"), dtype=t.float32, device="cuda")
+    o = t.empty((B, S_q, H, 128), dtype=t.bfloat16, device="cuda")
+    steps = [(150, None), (77, [77, 30]), (300, None), (64, [0, 0])]
+    for i, (n, lens) in enumerate(steps):
+        k = synth.normal_bf16((B, n, H, 128), 160 + i, 1)
+        v = synth.normal_bf16((B, n, H, 128), 170 + i, 1)
+        ld = None if lens is None else _lens_dev(lens)
+        _, k8, v8, akv = lsd.cast_qkv_fp8(to_dev(k), to_dev(k), to_dev(v), kv_lens=ld)
+        prev_o, prev_l = o_acc.cpu().numpy().astype(np.float64), lse_acc.cpu().numpy().astype(np.float64)
+        lsd.attn_fwd_fp8_accumulate(q8, k8, v8, aq[0], akv[1], akv[2], o_acc, lse_acc, o=o, kv_lens=ld)
+        t.cuda.synchronize()
+        new_o, new_l = o_acc.cpu().numpy().astype(np.float64), lse_acc.cpu().numpy().astype(np.float64)
+        ck, cv, ak, av = codes(k8), codes(v8), akv[1].cpu().numpy(), akv[2].cpu().numpy()
+        for b in range(B):
+            nb = n if lens is None else max(0, min(lens[b], n))
+            for h in range(H):
+                what = f"step {i} b={b} h={h}"
+                if nb == 0:
+                    assert np.array_equal(new_o[b, :, h], prev_o[b, :, h]) and np.array_equal(new_l[b, h], prev_l[b, h]), what
+                    continue
+                qh = deq_rows(cq, am_q, b, h)
+                kh = deq_rows(ck, ak, b, h)[:nb]
+                vh = deq_rows(cv, av, b, h)[:nb]
+                O_b, L_b = ref._attend_block(qh, kh, vh, sc)
+                s = (qh @ kh.T) * sc
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                l = p.sum(axis=1, keepdims=True)
+                bound_b = 2.0 ** -4 * (p @ np.abs(vh)) / l + 2.0 ** -10 * np.abs(vh).sum(axis=0)[None, :] / l
+                La = prev_l[b, h]
+                M = np.maximum(La, L_b)
+                with np.errstate(invalid="ignore"):
+                    wa = np.where(np.isneginf(La), 0.0, np.exp(La - M))
+                wb = np.exp(L_b - M)
+                Oa = np.where(np.isneginf(La)[:, None], 0.0, prev_o[b, :, h])
+                O_ref = (wa[:, None] * Oa + wb[:, None] * O_b) / (wa + wb)[:, None]
+                L_ref = M + np.log(wa + wb)
+                beta = (wb / (wa + wb))[:, None]
+                err = np.abs(new_o[b, :, h] - O_ref)
+                assert np.all(err <= beta * bound_b + 2.0 ** -8 * np.abs(O_ref) + 1e-5), \
+                    f"{what}: O outside the bound (ratio {float((err / (beta * bound_b + 2.0 ** -8 * np.abs(O_ref) + 1e-5)).max()):.3f})"
+                assert np.abs(new_l[b, h] - L_ref).max() <= 1e-3, f"{what}: LSE"
+        ob = o.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(ob - new_o) <= 2.0 ** -8 * np.abs(new_o) + 1e-30), f"step {i}: bf16 output"
