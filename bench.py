@@ -419,7 +419,8 @@ def leg_ring():
     import long_sequence_dit_amd as lsd
     B, Sb, H, D = 1, 25_200, 40, 128
     q, k, v = synth.qkv(B, Sb, 3 * Sb, H, D, seed=3)
-    dq, dk, dv = to_dev(q), to_dev(k), token_major(to_dev(v))
+    dq, dk, dvn = to_dev(q), to_dev(k), to_dev(v)
+    dv = token_major(dvn)
     del q, k, v
     out = {"workload": "Q [1,25200,40,128] vs K/V [1,75600,40,128] (seed 3, V token-contiguous) as 3 blocks of "
                        "25200: 3 x attention with fp32 LSE -> merge (n=3); unblocked attention; 3 fused Ring steps "
@@ -456,6 +457,43 @@ def leg_ring():
     out["ring_step_ms"] = {"blocks_plus_merge": round(ring_ms, 4), "fused_streaming": round(stream_ms, 4),
                            "TFLOP/s_blocks_plus_merge": round(3 * flop_blk / (ring_ms * 1e-3) / 1e12, 1),
                            "TFLOP/s_fused_streaming": round(3 * flop_blk / (stream_ms * 1e-3) / 1e12, 1)}
+    # The same share on the FP8 path: Q cast once, each K/V block cast with its
+    # own scales (so the logit factor is not a power of two for every block and
+    # the FP8 kernel applies it per score), then either three FP8 attentions
+    # and the merge, or three fused FP8 Ring steps.
+    qb = lsd.fp8_buffers(B, Sb, H, D)
+    lsd.cast_qkv_fp8(dq, dq, dq, out=qb)
+    kvb = []
+    for i in range(3):
+        bb = lsd.fp8_buffers(B, Sb, H, D)
+        lsd.cast_qkv_fp8(dk[:, i * Sb:(i + 1) * Sb], dk[:, i * Sb:(i + 1) * Sb], dvn[:, i * Sb:(i + 1) * Sb], out=bb)
+        kvb.append(bb)
+    q8, aq = qb[0], qb[3]
+    f8_blocks, f8_steps = {}, {}
+    for i in range(3):
+        bb = kvb[i]
+        f8_blocks[str(i)] = attn_leg(lambda bb=bb, i=i: lsd.attn_fwd_fp8(q8, bb[1], bb[2], aq[0], bb[3][1], bb[3][2],
+                                                                         o=parts[i], lse=lses[i]),
+                                     flop_blk, peak=PEAK_FP8_TFLOPS)
+    for i in range(3):
+        bb = kvb[i]
+        if i == 0:
+            def fn(bb=bb):
+                lse_acc.fill_(float("-inf"))
+                lsd.attn_fwd_fp8_accumulate(q8, bb[1], bb[2], aq[0], bb[3][1], bb[3][2], o_acc, lse_acc)
+        else:
+            def fn(bb=bb, i=i):
+                lsd.attn_fwd_fp8_accumulate(q8, bb[1], bb[2], aq[0], bb[3][1], bb[3][2], o_acc, lse_acc,
+                                            o=om if i == 2 else None)
+        f8_steps[str(i)] = attn_leg(fn, flop_blk, peak=PEAK_FP8_TFLOPS)
+    f8_ring = sum(b["median_ms"] for b in f8_blocks.values()) + out["attn_merge"]["median_ms"]
+    f8_stream = sum(x["median_ms"] for x in f8_steps.values())
+    out["fp8"] = {"workload": "the same share with Q and each K/V block cast to FP8 (E4M3, per-block scales): "
+                              "3 x FP8 attention -> merge (n=3), or 3 fused FP8 Ring steps",
+                  "attn_fwd_fp8_blocks": f8_blocks, "attn_fwd_fp8_accumulate_steps": f8_steps,
+                  "ring_step_ms": {"blocks_plus_merge": round(f8_ring, 4), "fused_streaming": round(f8_stream, 4),
+                                   "TFLOP/s_blocks_plus_merge": round(3 * flop_blk / (f8_ring * 1e-3) / 1e12, 1),
+                                   "TFLOP/s_fused_streaming": round(3 * flop_blk / (f8_stream * 1e-3) / 1e12, 1)}}
     return out
 
 
