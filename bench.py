@@ -458,15 +458,15 @@ def leg_ring():
                            "TFLOP/s_blocks_plus_merge": round(3 * flop_blk / (ring_ms * 1e-3) / 1e12, 1),
                            "TFLOP/s_fused_streaming": round(3 * flop_blk / (stream_ms * 1e-3) / 1e12, 1)}
     # The same share on the FP8 path: Q cast once, each K/V block cast with its
-    # own scales (so the logit factor is not a power of two for every block and
-    # the FP8 kernel applies it per score), then either three FP8 attentions
+    # own scales, K's chosen against Q's (lsd_cast_kv_fp8) so that every
+    # block's logit factor is a power of two, then either three FP8 attentions
     # and the merge, or three fused FP8 Ring steps.
     qb = lsd.fp8_buffers(B, Sb, H, D)
     lsd.cast_qkv_fp8(dq, dq, dq, out=qb)
     kvb = []
     for i in range(3):
         bb = lsd.fp8_buffers(B, Sb, H, D)
-        lsd.cast_qkv_fp8(dk[:, i * Sb:(i + 1) * Sb], dk[:, i * Sb:(i + 1) * Sb], dvn[:, i * Sb:(i + 1) * Sb], out=bb)
+        lsd.cast_kv_fp8(dk[:, i * Sb:(i + 1) * Sb], dvn[:, i * Sb:(i + 1) * Sb], qb[3][0], out=bb)
         kvb.append(bb)
     q8, aq = qb[0], qb[3]
     f8_blocks, f8_steps = {}, {}
@@ -488,8 +488,8 @@ def leg_ring():
         f8_steps[str(i)] = attn_leg(fn, flop_blk, peak=PEAK_FP8_TFLOPS)
     f8_ring = sum(b["median_ms"] for b in f8_blocks.values()) + out["attn_merge"]["median_ms"]
     f8_stream = sum(x["median_ms"] for x in f8_steps.values())
-    out["fp8"] = {"workload": "the same share with Q and each K/V block cast to FP8 (E4M3, per-block scales): "
-                              "3 x FP8 attention -> merge (n=3), or 3 fused FP8 Ring steps",
+    out["fp8"] = {"workload": "the same share with Q and each K/V block cast to FP8 (E4M3, per-block scales, K's "
+                              "chosen against Q's): 3 x FP8 attention -> merge (n=3), or 3 fused FP8 Ring steps",
                   "attn_fwd_fp8_blocks": f8_blocks, "attn_fwd_fp8_accumulate_steps": f8_steps,
                   "ring_step_ms": {"blocks_plus_merge": round(f8_ring, 4), "fused_streaming": round(f8_stream, 4),
                                    "TFLOP/s_blocks_plus_merge": round(3 * flop_blk / (f8_ring * 1e-3) / 1e12, 1),

@@ -14,6 +14,7 @@
  *   lsd_attn_fwd_fp8          attention on the FP8 inputs
  *   lsd_cast_qkv_fp8_masked   the cast with a per-batch key count
  *   lsd_attn_fwd_fp8_masked   FP8 attention with a per-batch key count
+ *   lsd_cast_kv_fp8           the FP8 cast of one K/V block for a Q cast earlier
  *   lsd_attn_fwd_fp8_accumulate  FP8 attention against one K/V block, merged
  *                             in place into a running (O, LSE) (Ring step)
  *   lsd_relayout_head_to_seq  head-major slices -> seq-major shard (Ulysses,
@@ -59,8 +60,9 @@ extern "C" {
 /* 2: lsd_cast_qkv_fp8 stores Q's scale amax (a power-of-two logit factor)
  *    in place of Q's plain amax; signatures unchanged from 1.
  * 3: adds lsd_cast_qkv_fp8_masked and lsd_attn_fwd_fp8_masked (the key-length
- *    mask on the FP8 path) and lsd_attn_fwd_fp8_accumulate (the fused Ring
- *    step on FP8 inputs); earlier entry points unchanged. */
+ *    mask on the FP8 path), lsd_attn_fwd_fp8_accumulate (the fused Ring step
+ *    on FP8 inputs) and lsd_cast_kv_fp8 (the cast of one K/V block against a
+ *    given Q scale); earlier entry points unchanged. */
 #define LSD_ABI_VERSION 3
 
 typedef enum lsd_status {
@@ -323,6 +325,29 @@ lsd_status lsd_attn_fwd_fp8_masked(const lsd_view4* q8, const lsd_view4* k8, con
  * The block's own result carries the FP8 error of lsd_attn_fwd_fp8; the merge
  * is the float32 arithmetic of lsd_attn_fwd_accumulate.
  */
+/*
+ * The FP8 cast of one key/value block for a query cast earlier (a Ring step's
+ * block): as lsd_cast_qkv_fp8 (or lsd_cast_qkv_fp8_masked with kv_lens) for K
+ * and V, except that Q is not cast and K's scale amax, not Q's, is adjusted:
+ * the smallest value amax_k' >= max |k| for which
+ * log2(e)/sqrt(128) * (q_scale_amax/448) * (amax_k'/448) is a power of two
+ * (the rule of lsd_cast_qkv_fp8 for Q with the two roles swapped; the factor
+ * is symmetric in them).  With it, lsd_attn_fwd_fp8 at the default softmax
+ * scale applies the logit factor exactly on the matrix cores for every block,
+ * although each block has its own scales.
+ *
+ *   src           2 bf16 views (B, S, H, D): K, V of the block, one shape
+ *   dst           2 FP8 views as dst[1] and dst[2] of lsd_cast_qkv_fp8
+ *   amax          float32 [3, B, H], written: [0] zero (no Q), [1] K's scale
+ *                 amax, [2] V's amax
+ *   q_scale_amax  float32 [B, H], not NULL: the query's scale amax (amax[0]
+ *                 of the query's lsd_cast_qkv_fp8)
+ *   kv_lens       NULL, or the block's valid keys per batch entry (as for
+ *                 lsd_cast_qkv_fp8_masked)
+ */
+lsd_status lsd_cast_kv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, const float* q_scale_amax,
+                           const int32_t* kv_lens, void* stream);
+
 lsd_status lsd_attn_fwd_fp8_accumulate(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8,
                                        const float* q_amax, const float* k_amax, const float* v_amax,
                                        const int32_t* kv_lens, float* o_acc, float* lse_acc, const lsd_view4* o,

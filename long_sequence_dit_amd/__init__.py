@@ -70,6 +70,9 @@ def lib():
         L.lsd_attn_fwd_fp8_masked.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, P(View4), ctypes.c_void_p,
                                               ctypes.c_float, ctypes.c_void_p]
+        L.lsd_cast_kv_fp8.restype = ctypes.c_int
+        L.lsd_cast_kv_fp8.argtypes = [P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
         L.lsd_attn_fwd_fp8_accumulate.restype = ctypes.c_int
         L.lsd_attn_fwd_fp8_accumulate.argtypes = [P(View4), P(View4), P(View4), ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -285,6 +288,24 @@ def cast_qkv_fp8(q, k, v, out=None, kv_lens=None):
         st = lib().lsd_cast_qkv_fp8_masked(sv, dv, ap, _lens_ptr(kv_lens, B), _stream(q))
         _check(st, "lsd_cast_qkv_fp8_masked")
     return q8, k8, v8, amax
+
+
+def cast_kv_fp8(k, v, q_scale_amax, out=None, kv_lens=None):
+    """The FP8 cast of one K/V block for a query cast earlier: K's scale amax is
+    chosen against ``q_scale_amax`` (float32 [B, H], the query cast's amax[0])
+    so that the default logit factor is a power of two.  Returns (k8, v8,
+    amax) with amax [3, B, H] ([0] zero, [1] K's scale amax, [2] V's);
+    ``out`` may be ``fp8_buffers(...)`` (its q8 is left untouched)."""
+    B, S, H, D = k.shape
+    if out is None:
+        out = fp8_buffers(B, S, H, D, k.device)
+    _, k8, v8, amax = out
+    sv = (View4 * 2)(_view(k, "k"), _view(v, "v"))
+    dv = (View4 * 2)(_view8(k8, "k8"), _view8(v8, "v8"))
+    st = lib().lsd_cast_kv_fp8(sv, dv, _f32_ptr(amax, "amax", (3, B, H)), _f32_ptr(q_scale_amax, "q_scale_amax", (B, H)),
+                               _lens_ptr(kv_lens, B), _stream(k))
+    _check(st, "lsd_cast_kv_fp8")
+    return k8, v8, amax
 
 
 def attn_fwd_fp8(q8, k8, v8, q_amax, k_amax, v_amax, o=None, lse=None, scale: Optional[float] = None,

@@ -247,19 +247,27 @@ lsd_status attention(bool acc, const lsd_view4* q, const lsd_view4* k, const lsd
   return launched(lsd::launch_attn_fwd(a, (hipStream_t)stream), acc ? "attn_fwd_accumulate" : "attn_fwd");
 }
 
+// q_scale != nullptr: the K/V-only cast (slot 0 repeats slot 1 and is neither
+// read nor written; K's scale amax is chosen against the given Q scales).
 lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, const int32_t* kv_lens,
-                        void* stream) {
+                        const float* q_scale, void* stream) {
   if (src == nullptr || dst == nullptr) return fail(LSD_EINVAL, "null src or dst array");
   lsd_status s;
+  const int t0 = q_scale != nullptr ? 1 : 0;
   static const char* sn[3] = {"src[0] (q)", "src[1] (k)", "src[2] (v)"};
   static const char* dn[3] = {"dst[0] (q8)", "dst[1] (k8)", "dst[2] (v8, transposed)"};
-  for (int t = 0; t < 3; ++t) {
-    if ((s = check_view(sn[t], &src[t])) != LSD_OK) return s;
-    if ((s = check_view8(dn[t], &dst[t], t == 2 ? 1 : 3)) != LSD_OK) return s;
-    if (!same_shape(src[t], src[0])) return fail(LSD_EINVAL, "%s: q, k and v must have one shape", sn[t]);
-    if (!same_shape(dst[t], src[0])) return fail(LSD_EINVAL, "%s: shape must equal the sources' (B, S, H, D)", dn[t]);
+  static const char* snk[3] = {"", "src[0] (k)", "src[1] (v)"};
+  static const char* dnk[3] = {"", "dst[0] (k8)", "dst[1] (v8, transposed)"};
+  const char* const* sn_ = t0 ? snk : sn;
+  const char* const* dn_ = t0 ? dnk : dn;
+  for (int t = t0; t < 3; ++t) {
+    if ((s = check_view(sn_[t], &src[t])) != LSD_OK) return s;
+    if ((s = check_view8(dn_[t], &dst[t], t == 2 ? 1 : 3)) != LSD_OK) return s;
+    if (!same_shape(src[t], src[t0])) return fail(LSD_EINVAL, "%s: the sources must have one shape", sn_[t]);
+    if (!same_shape(dst[t], src[t0]))
+      return fail(LSD_EINVAL, "%s: shape must equal the sources' (B, S, H, D)", dn_[t]);
   }
-  const int64_t B = src[0].shape[0], S = src[0].shape[1], H = src[0].shape[2], D = src[0].shape[3];
+  const int64_t B = src[t0].shape[0], S = src[t0].shape[1], H = src[t0].shape[2], D = src[t0].shape[3];
   if (D != 128) return fail(LSD_EUNSUPPORTED, "FP8 path: head dim D=%lld unsupported (128)", (long long)D);
   // V rows are written up to the next multiple of 64 tokens (zero codes)
   const int64_t s_pad = (S + 63) / 64 * 64;
@@ -269,19 +277,22 @@ lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax,
   if (amax == nullptr) return fail(LSD_EINVAL, "null amax");
   if ((uintptr_t)amax % 4 != 0) return fail(LSD_EINVAL, "amax not 4-byte aligned");
   if (kv_lens != nullptr && (uintptr_t)kv_lens % 4 != 0) return fail(LSD_EINVAL, "kv_lens not 4-byte aligned");
+  if (q_scale != nullptr && (uintptr_t)q_scale % 4 != 0) return fail(LSD_EINVAL, "q_scale_amax not 4-byte aligned");
   if (B * H == 0) return ok();
-  Span ins[4], outs[4];
+  Span ins[5], outs[4];
+  const Span none = span_flat(nullptr, 0, 1);
   for (int t = 0; t < 3; ++t) {
-    ins[t] = span_of(src[t], 2);
-    outs[t] = span_of(dst[t], 1);
+    ins[t] = t >= t0 ? span_of(src[t], 2) : none;
+    outs[t] = t >= t0 ? span_of(dst[t], 1) : none;
   }
   ins[3] = span_flat(kv_lens, B, 4);
+  ins[4] = span_flat(q_scale, B * H, 4);
   outs[2].hi += (uintptr_t)(s_pad - S);  // the last row's padding is written too
   outs[3] = span_flat(amax, 3 * B * H, 4);
-  const char* on[4] = {dn[0], dn[1], dn[2], "amax"};
-  const char* in_names[4] = {sn[0], sn[1], sn[2], "kv_lens"};
+  const char* on[4] = {dn_[0], dn_[1], dn_[2], "amax"};
+  const char* in_names[5] = {sn_[0], sn_[1], sn_[2], "kv_lens", "q_scale_amax"};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 5; ++j)
       if (overlaps(outs[i], ins[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], in_names[j]);
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outs[j])) return fail(LSD_EINVAL, "%s overlaps %s", on[i], on[j]);
@@ -298,8 +309,9 @@ lsd_status cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax,
   a.dst_sd_v = dst[2].stride[3];
   a.amax = amax;
   a.kv_lens = kv_lens;
+  a.q_scale_in = q_scale;
   a.B = (int)B; a.S = (int)S; a.H = (int)H;
-  return launched(lsd::launch_cast_fp8(a, (hipStream_t)stream), "cast_qkv_fp8");
+  return launched(lsd::launch_cast_fp8(a, (hipStream_t)stream), q_scale ? "cast_kv_fp8" : "cast_qkv_fp8");
 }
 
 lsd_status attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,
@@ -571,13 +583,22 @@ lsd_status relayout(bool inverse, const char* fn, int n_tensors, int P, int rank
 extern "C" {
 
 lsd_status lsd_cast_qkv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, void* stream) {
-  return cast_qkv_fp8(src, dst, amax, nullptr, stream);
+  return cast_qkv_fp8(src, dst, amax, nullptr, nullptr, stream);
+}
+
+lsd_status lsd_cast_kv_fp8(const lsd_view4* src, const lsd_view4* dst, float* amax, const float* q_scale_amax,
+                           const int32_t* kv_lens, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(LSD_EINVAL, "null src or dst array");
+  if (q_scale_amax == nullptr) return fail(LSD_EINVAL, "null q_scale_amax");
+  const lsd_view4 s3[3] = {src[0], src[0], src[1]};
+  const lsd_view4 d3[3] = {dst[0], dst[0], dst[1]};
+  return cast_qkv_fp8(s3, d3, amax, kv_lens, q_scale_amax, stream);
 }
 
 lsd_status lsd_cast_qkv_fp8_masked(const lsd_view4* src, const lsd_view4* dst, float* amax, const int32_t* kv_lens,
                                    void* stream) {
   if (kv_lens == nullptr) return fail(LSD_EINVAL, "null kv_lens");
-  return cast_qkv_fp8(src, dst, amax, kv_lens, stream);
+  return cast_qkv_fp8(src, dst, amax, kv_lens, nullptr, stream);
 }
 
 lsd_status lsd_attn_fwd_fp8(const lsd_view4* q8, const lsd_view4* k8, const lsd_view4* v8, const float* q_amax,

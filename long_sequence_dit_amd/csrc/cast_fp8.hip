@@ -55,7 +55,8 @@ __device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
 // Tokens of tensor t of batch entry b that count: all S for Q, the first
 // kv_lens[b] (clamped to [0, S]) for K and V under the key-length mask.
 __device__ inline int valid_tokens(const CastArgs& a, int t, int b) {
-  if (t == 0 || a.kv_lens == nullptr) return a.S;
+  if (t == 0) return a.q_scale_in != nullptr ? 0 : a.S;  // no Q in the K/V-only cast
+  if (a.kv_lens == nullptr) return a.S;
   return min(max(a.kv_lens[b], 0), a.S);
 }
 
@@ -128,10 +129,14 @@ __device__ inline float q_scale_amax(float aq, float ak) {
   return (r <= 3.402823466e38f) ? r : aq;
 }
 
-// the factor that codes tensor t of (b, h): 448 / amax, Q's from its scale amax
+// the factor that codes tensor t of (b, h): 448 / amax, Q's from its scale
+// amax; in the K/V-only cast K's from its scale amax against the given Q's
+// (the logit factor is symmetric in the two scales, so the same rule applies)
 __device__ inline float code_factor(const CastArgs& a, int t, int64_t bh) {
   const float am = a.amax[(int64_t)t * a.B * a.H + bh];
-  return inv_scale(t == 0 ? q_scale_amax(am, a.amax[(int64_t)a.B * a.H + bh]) : am);
+  if (t == 0) return inv_scale(q_scale_amax(am, a.amax[(int64_t)a.B * a.H + bh]));
+  if (t == 1 && a.q_scale_in != nullptr) return inv_scale(q_scale_amax(am, a.q_scale_in[bh]));
+  return inv_scale(am);
 }
 
 // Per-head Q and K pass (any strides; contiguous tensors with contiguous code
@@ -199,9 +204,15 @@ __global__ void __launch_bounds__(256) quant_vt_kernel(const CastArgs a, int n_c
   const int lim = valid_tokens(a, 2, b);  // tokens past it code as zero
   // Q's stored amax becomes its scale amax; the Q pass (an earlier launch)
   // has finished reading it
+  // (in the K/V-only cast K's stored amax becomes its scale amax instead)
   if (chunk == 0 && threadIdx.x == 0) {
-    float* aq = &a.amax[(int64_t)b * a.H + h];
-    *aq = q_scale_amax(*aq, a.amax[((int64_t)a.B + b) * a.H + h]);
+    if (a.q_scale_in == nullptr) {
+      float* aq = &a.amax[(int64_t)b * a.H + h];
+      *aq = q_scale_amax(*aq, a.amax[((int64_t)a.B + b) * a.H + h]);
+    } else {
+      float* ak = &a.amax[((int64_t)a.B + b) * a.H + h];
+      *ak = q_scale_amax(*ak, a.q_scale_in[(int64_t)b * a.H + h]);
+    }
   }
   const int tid = threadIdx.x;
   const int g = tid >> 4;      // token group (0..15)

@@ -95,6 +95,10 @@ struct CastArgs {
   // [0, S]): K and V amax over those only, V codes of the rest zero, K codes
   // of the rest not written
   const int32_t* kv_lens;
+  // null, or the K/V-only cast: Q (slot 0) is neither read nor written and its
+  // amax stays 0; K's scale amax is chosen against these Q scale amaxes [B, H]
+  // (the power-of-two rule of Q's scale, with the roles swapped)
+  const float* q_scale_in;
   int B, S, H;
 };
 hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t stream);

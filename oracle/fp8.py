@@ -163,6 +163,27 @@ def cast_qkv(q, k, v, kv_lens=None):
     return q8, k8, v8, amax
 
 
+def cast_kv(k, v, q_scale, kv_lens=None):
+    """The FP8 cast of one key/value block for a query cast earlier: codes of K
+    and V and the amax array [3, B, H] ([0] zero: no Q; [1] K's scale amax, the
+    ``q_scale_amax`` rule with the roles of Q and K swapped, against the given
+    Q scale amax [B, H]; [2] V's amax).  ``kv_lens`` as for ``cast_qkv``."""
+    if kv_lens is None:
+        ak, av = head_amax(k), head_amax(v)
+        lens = None
+    else:
+        lens = valid_lengths(kv_lens, np.asarray(k).shape[0], np.asarray(k).shape[1])
+        ak, av = head_amax_valid(k, lens), head_amax_valid(v, lens)
+    amax = np.stack([np.zeros_like(ak), ak, av]).astype(np.float32)
+    amax[1] = q_scale_amax(amax[1], np.asarray(q_scale, dtype=np.float32))
+    with np.errstate(invalid="ignore"):
+        k8, v8 = quantize(k, amax[1]), quantize(v, amax[2])
+    if lens is not None:
+        for b in range(v8.shape[0]):
+            v8[b, lens[b]:] = 0
+    return k8, v8, amax
+
+
 def dequantize(codes, amax) -> np.ndarray:
     """decode(code) * (amax / 448), the scale applied in float32."""
     s = (np.asarray(amax, dtype=np.float32) / np.float32(E4M3_MAX)).astype(np.float32)

@@ -678,6 +678,36 @@ def pin_fp8_ring_steps():
     assert np.array_equal(o2, o) and np.array_equal(l2, lse)
 
 
+def pin_fp8_kv_cast():
+    """The K/V-only cast against a given Q scale: K's scale amax lies in
+    [amax_k, 2 amax_k) and with it the default logit factor
+    log2(e) / sqrt(128) * (q_scale / 448) * (k_scale / 448) is a power of two
+    (float64, to 2^-20); K is coded with it, V exactly as the full cast codes
+    it; slot 0 is zero; with a key-length mask V's padding codes are zero and
+    the scales come from the valid tokens."""
+    from oracle import fp8
+    B, S, H, D = 2, 45, 3, 64
+    q = _rand((B, S, H, D), 91)
+    k = _rand((B, S, H, D), 92)
+    v = _rand((B, S, H, D), 93)
+    _, _, _, aq = fp8.cast_qkv(q, q, q)
+    k8, v8, amax = fp8.cast_kv(k, v, aq[0])
+    ak = fp8.head_amax(k).astype(np.float64)
+    a1 = amax[1].astype(np.float64)
+    assert np.all(amax[0] == 0)
+    assert np.all(a1 >= ak) and np.all(a1 < 2.0 * ak * (1.0 + 2.0 ** -20))
+    lg = np.log2((np.log2(np.e) / np.sqrt(128.0)) * (aq[0].astype(np.float64) / 448.0) * (a1 / 448.0))
+    assert np.all(np.abs(lg - np.round(lg)) < 2.0 ** -20 / np.log(2.0))
+    assert np.array_equal(k8, fp8.quantize(k, amax[1]))
+    _, _, fv8, famax = fp8.cast_qkv(q, k, v)
+    assert np.array_equal(v8, fv8) and np.array_equal(amax[2], famax[2])
+    lens = [45, 7]
+    mk8, mv8, mamax = fp8.cast_kv(k, v, aq[0], kv_lens=lens)
+    _, _, mfv8, mfamax = fp8.cast_qkv(q, k, v, kv_lens=lens)
+    assert np.array_equal(mv8, mfv8) and np.array_equal(mamax[2], mfamax[2])
+    assert np.array_equal(mamax[1], fp8.q_scale_amax(mfamax[1], aq[0]))
+
+
 FP8_PINS = [pin_e4m3_code_table, pin_e4m3_rounding, pin_fp8_cast, pin_fp8_q_scale, pin_fp8_attention,
-            pin_fp8_key_lengths, pin_fp8_ring_steps]
+            pin_fp8_key_lengths, pin_fp8_ring_steps, pin_fp8_kv_cast]
 ALL_PINS = ALL_PINS + FP8_PINS

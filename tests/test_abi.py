@@ -354,6 +354,31 @@ def test_fp8_masked_entry_points_validation():
     assert r == LSD_EINVAL and "overlaps" in msg
 
 
+def test_fp8_kv_cast_validation():
+    """The K/V-only cast: q_scale_amax must be given and aligned and may not
+    overlap an output; K and V must have one shape."""
+    L = lsd.lib()
+    B, S, H, D = 2, 100, 3, 128
+    src = [view(BASE + t * GB, (B, S, H, D)) for t in range(2)]
+    k8 = view8(BASE + 11 * GB, (B, S, H, D), [S * H * D, H * D, D, 1])
+    v8 = view8(BASE + 12 * GB, (B, S, H, D), [H * D * 128, 1, D * 128, 128])
+    amax, qs = BASE + 13 * GB, BASE + 14 * GB
+
+    def cast(sv, dv, q):
+        r = L.lsd_cast_kv_fp8((View4 * 2)(*sv), (View4 * 2)(*dv), ctypes.c_void_p(amax),
+                              ctypes.c_void_p(q) if q else None, None, None)
+        return r, L.lsd_last_error().decode()
+
+    r, msg = cast(src, [k8, v8], 0)
+    assert r == LSD_EINVAL and "null q_scale_amax" in msg
+    r, msg = cast(src, [k8, v8], qs + 2)
+    assert r == LSD_EINVAL and "q_scale_amax not 4-byte aligned" in msg
+    r, msg = cast(src, [k8, v8], amax + 8)
+    assert r == LSD_EINVAL and "amax overlaps q_scale_amax" in msg
+    r, msg = cast([src[0], view(BASE + GB, (B, S + 1, H, D))], [k8, v8], qs)
+    assert r == LSD_EINVAL and "one shape" in msg
+
+
 def test_fp8_accumulate_validation():
     """The FP8 Ring step: o_acc and lse_acc must be given and aligned, and no
     output (o_acc, lse_acc, o) may overlap an input or another output."""

@@ -311,7 +311,43 @@ def test_masked_attention_within_fp8_contract(S, H):
 
 # ------------------------------------------------ fused Ring step (FP8 path)
 
-def test_fp8_ring_steps_within_contract():
+@pytest.mark.parametrize("layout,masked", [("contiguous", False), ("contiguous", True), ("fused", True)])
+def test_kv_cast_bit_exact(layout, masked):
+    """lsd_cast_kv_fp8: K's scale amax chosen against a given Q scale, codes
+    and all three amax slots bit-exact against the oracle; the q8 buffer of
+    ``out`` untouched; with the key-length mask the padding as in the masked
+    cast (NaN there, V codes zero, K codes not written)."""
+    note(f"fp8 K/V-only cast ({layout}, masked={masked})")
+    t = torch()
+    S, H = 300, 3
+    lens = MASK_LENS if masked else [S] * len(MASK_LENS)
+    q, k, v = _poisoned_qkv(lens, S, H, 190)
+    B = len(lens)
+    dq = to_dev(q)
+    _, _, _, aq = lsd.cast_qkv_fp8(dq, dq, dq)
+    if layout == "fused":
+        f = to_dev(np.stack([k, v, v], axis=2))
+        dk, dv = f[:, :, 0], f[:, :, 1]
+    else:
+        dk, dv = to_dev(k), to_dev(v)
+    out = lsd.fp8_buffers(B, S, H)
+    out[0].view(t.uint8).fill_(0x33)
+    out[1].view(t.uint8).fill_(0x5A)
+    k8, v8, amax = lsd.cast_kv_fp8(dk, dv, aq[0], out=out, kv_lens=_lens_dev(lens) if masked else None)
+    t.cuda.synchronize()
+    ek8, ev8, eamax = fp8.cast_kv(k, v, aq[0].cpu().numpy(), kv_lens=lens if masked else None)
+    assert np.array_equal(amax.cpu().numpy(), eamax), "amax"
+    assert np.all(codes(out[0]) == 0x33), "q8 written"
+    gk = codes(k8)
+    for b, n in enumerate(lens):
+        n = max(0, min(n, S))
+        assert np.array_equal(gk[b, :n], ek8[b, :n]), f"k codes b={b}"
+        assert np.all(gk[b, n:] == 0x5A), f"k padding written b={b}"
+    assert np.array_equal(codes(v8), ev8), "v codes"
+
+
+@pytest.mark.parametrize("kv_cast", [False, True])
+def test_fp8_ring_steps_within_contract(kv_cast):
     """lsd_attn_fwd_fp8_accumulate over four K/V blocks (each cast with its
     own scales; one with a key-length mask, one whose every entry is empty),
     each step checked from the GPU's own prior state: the merged O within the
@@ -319,7 +355,7 @@ def test_fp8_ring_steps_within_contract():
     w_b / (w_acc + w_b) (plus float32 merge rounding), the LSE within 1e-3,
     an empty block leaving the running result bit-identical, and the bf16
     output the running O rounded."""
-    note("fp8 fused Ring steps")
+    note(f"fp8 fused Ring steps (blocks cast against the Q scale: {kv_cast})")
     t = torch()
     B, S_q, H = 2, 200, 2
     sc = ref._default_scale(128, None)
@@ -335,7 +371,10 @@ def test_fp8_ring_steps_within_contract():
         k = synth.normal_bf16((B, n, H, 128), 160 + i, 1)
         v = synth.normal_bf16((B, n, H, 128), 170 + i, 1)
         ld = None if lens is None else _lens_dev(lens)
-        _, k8, v8, akv = lsd.cast_qkv_fp8(to_dev(k), to_dev(k), to_dev(v), kv_lens=ld)
+        if kv_cast:  # each block's K scale chosen against Q's: the power-of-two path
+            k8, v8, akv = lsd.cast_kv_fp8(to_dev(k), to_dev(v), aq[0], kv_lens=ld)
+        else:
+            _, k8, v8, akv = lsd.cast_qkv_fp8(to_dev(k), to_dev(k), to_dev(v), kv_lens=ld)
         prev_o, prev_l = o_acc.cpu().numpy().astype(np.float64), lse_acc.cpu().numpy().astype(np.float64)
         lsd.attn_fwd_fp8_accumulate(q8, k8, v8, aq[0], akv[1], akv[2], o_acc, lse_acc, o=o, kv_lens=ld)
         t.cuda.synchronize()
